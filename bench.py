@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of the k-bit weight-quantized matmul on one MI355X.
+
+Workload (one "step"): the decode product Y[1, 11008] = x[1, 4096] . dequant(Wq)
+for 7B-MLP-shaped weights at k = 3, 4 and 6 bits, G = 128 (three qmm_gemv
+launches).  Inputs are seeded synthetic data already resident in HBM; each
+launch reads its own copy of the packed weights and scales out of a rotating
+set larger than 1 GiB, so no launch finds its weights in the 256 MB Infinity
+Cache or the L2 (the pages' protocol clears the cache between runs; here every
+launch simply reads weights nothing else has touched recently).
+
+Timing: HIP events recorded on the launch stream around every launch (the
+stream is first held by a spin kernel so the whole timed region is queued
+before the GPU starts it).  `value` is packed-weight bytes per second over the
+timed region; the `roofline` object prices the dominant kernel's algorithmic
+bytes (packed weights + scales + x + y) per launch against its mean launch
+duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
+prefill product (qmm_gemm) in TFLOP/s against the 2.5 PFLOP/s dense fp16 MFMA
+peak, and the CPU oracle timed on this host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFS = 2516.6    # MI355X dense fp16 MFMA, published (2.5 PFLOP/s)
+INT8_MFMA_PEAK_TOPS = 5033.2
+METRIC = "packed-weight HBM GB/s (% peak) at M=1; TFLOP/s (% MFMA peak) at M=2048"
+ROTATE_BYTES = 1 << 30
+PROFILE_TRAFFIC = os.path.join(HERE, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--suite", action="store_true", help="also print one line per parity workload")
+    ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "bit_weight_quantized_qmm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".inc")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """Per-launch HIP events on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def hold(self):
+        # keep the stream busy while the host queues the timed launches
+        self.torch.cuda._sleep(200_000_000)
+
+    def launch(self, key, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.pairs.setdefault(key, []).append((ev0, ev1))
+
+    def mean_ms(self, key):
+        p = self.pairs[key]
+        return sum(a.elapsed_time(b) for a, b in p) / len(p)
+
+    def span_ms(self, keys):
+        firsts = [self.pairs[k][0][0] for k in keys]
+        lasts = [self.pairs[k][-1][1] for k in keys]
+        first = firsts[0]
+        return max(first.elapsed_time(l) for l in lasts)
+
+
+def decode_setup(torch, q, synthetic, bits):
+    w = synthetic.DECODE_7B
+    c = synthetic.make_case(1, w["K"], w["N"], bits, w["G"], synthetic.seed_for(2, bits), s_range=w["s_range"])
+    dev = "cuda:0"
+    wq0 = q.pack(torch.from_numpy(c["codes"]).to(dev), bits)
+    s0 = torch.from_numpy(c["s"]).to(dev)
+    per = wq0.numel() * 4 + s0.numel() * 2
+    copies = max(2, -(-ROTATE_BYTES // per))
+    bufs = [(wq0.clone(), s0.clone()) for _ in range(copies)]
+    del wq0
+    x = torch.from_numpy(c["X"]).to(dev)
+    y = torch.empty((1, w["N"]), dtype=torch.float16, device=dev)
+    wq_bytes = w["N"] * w["K"] * bits // 8
+    alg = wq_bytes + s0.numel() * 2 + x.numel() * 2 + y.numel() * 2
+    return dict(bits=bits, bufs=bufs, x=x, y=y, K=w["K"], N=w["N"], G=w["G"], wq_bytes=wq_bytes, alg_bytes=alg,
+                case=c, i=0)
+
+
+def decode_launch(q, d):
+    wq, s = d["bufs"][d["i"] % len(d["bufs"])]
+    d["i"] += 1
+    q.gemv(d["x"], wq, s, None, d["bits"], d["G"], out=d["y"])
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    try:
+        with open(PROFILE_TRAFFIC) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    e = t.get("kernels", {}).get(kernel_key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def cpu_baseline(synthetic, budget_s=12.0):
+    """The oracle as it stands, timed on this host: the same decode step
+    (k = 3, 4, 6) repeated until about budget_s seconds have passed."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    orc = oracle.default()
+    w = synthetic.DECODE_7B
+    cases = []
+    for bits in w["bits"]:
+        c = synthetic.make_case(1, w["K"], w["N"], bits, w["G"], synthetic.seed_for(2, bits), s_range=w["s_range"])
+        cases.append((c, orc.pack(c["codes"], bits)))
+    done_bytes, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for c, st in cases:
+            orc.qmm(c["X"], st, c["s"], None, c["bits"], c["G"])
+            done_bytes += st.size
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x the full decode step (k=3,4,6; M=1 K=4096 N=11008): bit-serial unpack, "
+                      f"fp64 dequant and fp64 dot products, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported here "
+              f"(the product shards by output column, see the design notes).", file=sys.stderr)
+        return 2
+    import torch
+    import bit_weight_quantized_qmm_amd as q
+    import synthetic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    print(f"bench: setting up decode workload", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.int32, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copies": 3}))
+        return 0
+
+    decs = [decode_setup(torch, q, synthetic, bits) for bits in synthetic.DECODE_7B["bits"]]
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        for d in decs:
+            decode_launch(q, d)
+    torch.cuda.synchronize()
+    print(f"bench: timing {args.steps} decode steps", file=sys.stderr, flush=True)
+    timer.hold()
+    for _ in range(args.steps):
+        for d in decs:
+            timer.launch(("gemv", d["bits"]), lambda d=d: decode_launch(q, d))
+    torch.cuda.synchronize()
+    keys = [("gemv", d["bits"]) for d in decs]
+    span = timer.span_ms(keys)
+    ms_per_step = span / args.steps
+    wq_step = sum(d["wq_bytes"] for d in decs)
+    value = wq_step / (ms_per_step * 1e-3) / 1e9
+    per_bits = {}
+    for d in decs:
+        ms = timer.mean_ms(("gemv", d["bits"]))
+        per_bits[str(d["bits"])] = {
+            "us_per_launch": round(ms * 1e3, 3),
+            "packed_GBs": round(d["wq_bytes"] / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_GBs": round(d["alg_bytes"] / (ms * 1e-3) / 1e9, 1),
+            "packed_frac_of_peak": round(d["wq_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    dom = max(decs, key=lambda d: timer.mean_ms(("gemv", d["bits"])))
+    dom_ms = timer.mean_ms(("gemv", dom["bits"]))
+    achieved = dom["alg_bytes"] / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(f"gemv_m1_k{dom['bits']}"),
+                "kernel": f"qmm_gemv M=1 k={dom['bits']} (gemv_m1_kernel)",
+                "algorithmic_bytes_per_launch": dom["alg_bytes"]}
+    del decs
+    torch.cuda.empty_cache()
+
+    # prefill product on the MFMA path
+    print("bench: timing the M=2048 prefill product", file=sys.stderr, flush=True)
+    w = synthetic.PREFILL
+    c = synthetic.make_case(w["M"], w["K"], w["N"], 4, w["G"], synthetic.seed_for(4, 4), s_range=w["s_range"])
+    X = torch.from_numpy(c["X"]).to("cuda:0")
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
+    s = torch.from_numpy(c["s"]).to("cuda:0")
+    Y = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda:0")
+    for _ in range(3):
+        q.gemm(X, wq, s, None, 4, w["G"], out=Y)
+    torch.cuda.synchronize()
+    timer.hold()
+    nrep = max(10, args.steps // 2)
+    for _ in range(nrep):
+        timer.launch("gemm", lambda: q.gemm(X, wq, s, None, 4, w["G"], out=Y))
+    torch.cuda.synchronize()
+    gms = timer.mean_ms("gemm")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    tfs = flops / (gms * 1e-3) / 1e12
+    gemm = {"workload": w["name"], "us_per_launch": round(gms * 1e3, 2), "TFLOPs": round(tfs, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": traffic_for("gemm_k4")}}
+
+    cpu = None
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(synthetic)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": synthetic.DECODE_7B["name"] + " k{3,4,6}", "M": 1, "K": 4096, "N": 11008,
+                   "bits": [3, 4, 6], "G": 128, "launches_per_step": 3,
+                   "weights_read_from": "HBM (rotating copies > 1 GiB)"},
+        "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "per_bits": per_bits,
+        "gemm_m2048": gemm,
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,156 @@
+"""k-bit weight-quantized matmul on AMD MI355X (gfx950): Python binding of libqmm.so.
+
+This module only marshals arguments: it checks tensor dtypes, shapes and
+devices, passes raw device pointers and the current HIP stream to the C ABI
+(``include/qmm.h``) and raises :class:`QmmError` on a non-zero status.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  Importing the package fails loudly if ``libqmm.so`` has not been
+built (``python -m bit_weight_quantized_qmm_amd._build``).
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIBRARY
+
+__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "library_path", "SYMBOLS"]
+
+SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8",
+           "qmm_status_string", "qmm_last_error")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it first (python -m bit_weight_quantized_qmm_amd._build)")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "qmm_packed_bytes": ([I64, I64, INT], ctypes.c_size_t),
+        "qmm_pack": ([P, P, I64, I64, INT, P], INT),
+        "qmm_unpack": ([P, P, I64, I64, INT, P], INT),
+        "qmm_gemv": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_gemm_w4a8": ([P, P, P, P, P, P, P, I64, I64, I64, I64, P], INT),
+        "qmm_status_string": ([INT], ctypes.c_char_p),
+        "qmm_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def _check(status: int):
+    if status != 0:
+        raise QmmError(status, _lib.qmm_last_error().decode() or _lib.qmm_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def packed_bytes(K: int, N: int, bits: int) -> int:
+    return int(_lib.qmm_packed_bytes(K, N, bits))
+
+
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """uint8 codes [K, N] -> packed stream as int32 [N, K*bits/32] (bit pattern)."""
+    _need(codes, "codes", torch.uint8)
+    K, N = codes.shape
+    if out is None:
+        out = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
+    _need(out, "out", torch.int32, (N, K * bits // 32), codes.device)
+    _check(_lib.qmm_pack(_ptr(codes), _ptr(out), K, N, bits, _stream(codes.device)))
+    return out
+
+
+def unpack(wq: torch.Tensor, K: int, N: int, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed stream [N, K*bits/32] -> uint8 codes [K, N] through the kernels' register unpack."""
+    _need(wq, "wq", torch.int32, (N, K * bits // 32))
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.uint8, device=wq.device)
+    _need(out, "out", torch.uint8, (K, N), wq.device)
+    _check(_lib.qmm_unpack(_ptr(wq), _ptr(out), K, N, bits, _stream(wq.device)))
+    return out
+
+
+def _product(fn, X, wq, s, z, bits, G, out):
+    _need(X, "X", torch.float16)
+    M, K = X.shape
+    N = s.shape[0] if s.dim() == 2 else -1
+    _need(wq, "wq", torch.int32, (N, K * bits // 32), X.device)
+    _need(s, "s", torch.float16, (N, K // G), X.device)
+    if z is not None:
+        _need(z, "z", torch.float16, (N, K // G), X.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(out, "out", torch.float16, (M, N), X.device)
+    _check(fn(_ptr(X), _ptr(wq), _ptr(s), _ptr(z), _ptr(out), M, K, N, bits, G, _stream(X.device)))
+    return out
+
+
+def gemv(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
+    """Y [M, N] fp16 = X [M, K] fp16 . dequant(wq); 1 <= M <= 16."""
+    return _product(_lib.qmm_gemv, X, wq, s, z, bits, G, out)
+
+
+def gemm(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
+    """Y [M, N] fp16 = X [M, K] fp16 . dequant(wq); any M (f16 MFMA path)."""
+    return _product(_lib.qmm_gemm, X, wq, s, z, bits, G, out)
+
+
+def gemm_w4a8(Xq, sx, wq, s, z, G: int, out=None, acc_out=None) -> torch.Tensor:
+    """Y [M, N] fp16 for int8 activations Xq [M, K] with per-token fp16 scales sx [M] and
+    4-bit weights; acc_out (int32 [M, K/G, N]) optionally receives the exact group sums."""
+    _need(Xq, "Xq", torch.int8)
+    M, K = Xq.shape
+    N = s.shape[0]
+    _need(sx, "sx", torch.float16, (M,), Xq.device)
+    _need(wq, "wq", torch.int32, (N, K * 4 // 32), Xq.device)
+    _need(s, "s", torch.float16, (N, K // G), Xq.device)
+    if z is not None:
+        _need(z, "z", torch.float16, (N, K // G), Xq.device)
+    if acc_out is not None:
+        _need(acc_out, "acc_out", torch.int32, (M, K // G, N), Xq.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    _need(out, "out", torch.float16, (M, N), Xq.device)
+    _check(_lib.qmm_gemm_w4a8(_ptr(Xq), _ptr(sx), _ptr(wq), _ptr(s), _ptr(z), _ptr(out), _ptr(acc_out),
+                              M, K, N, G, _stream(Xq.device)))
+    return out

@@ -1,0 +1,137 @@
+// abi.cpp -- the C ABI declared in include/qmm.h: argument validation (host
+// only, before any HIP call), then one launch on the caller's stream.
+#include "../../include/qmm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+qmm_status fail(qmm_status st, const char *fmt, const char *what)
+{
+    snprintf(g_last_error, sizeof g_last_error, fmt, what);
+    return st;
+}
+
+// Largest sizes the kernels index with 32-bit arithmetic: with K <= 2^21 every
+// buffer resource the kernels build (at most 256 rows of X, 64 columns of Wq)
+// stays below 2^31 bytes, below the out-of-range offset they use for padding.
+constexpr int64_t kMaxK = int64_t(1) << 21;
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxM = int64_t(1) << 24;
+
+qmm_status check_shape(const char *fn, int64_t M, int64_t K, int64_t N, int bits, int64_t G, bool need_g)
+{
+    if (bits < 1 || bits > 8) return fail(QMM_ERR_INVALID_ARG, "%s: bits must be in 1..8", fn);
+    if (K < 32 || K % 32 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: K must be a positive multiple of 32", fn);
+    if (N < 1) return fail(QMM_ERR_INVALID_ARG, "%s: N must be >= 1", fn);
+    if (M < 1) return fail(QMM_ERR_INVALID_ARG, "%s: M must be >= 1", fn);
+    if (need_g && (G < 32 || G % 32 != 0 || K % G != 0))
+        return fail(QMM_ERR_INVALID_ARG, "%s: G must be a positive multiple of 32 dividing K", fn);
+    if (K > kMaxK || N > kMaxN || M > kMaxM)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: dimension beyond the supported range", fn);
+    if ((K / 32) * N > (int64_t(1) << 31) - 256)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: problem beyond the supported range", fn);
+    if (((M + 255) / 256) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: problem beyond the supported range", fn);
+    return QMM_OK;
+}
+
+qmm_status hip_status(hipError_t e, const char *fn)
+{
+    if (e == hipSuccess) {
+        g_last_error[0] = '\0';
+        return QMM_OK;
+    }
+    if (e == hipErrorNotSupported) return fail(QMM_ERR_UNSUPPORTED, "%s: shape not supported by the kernel", fn);
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", fn, hipGetErrorString(e));
+    return QMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmm_packed_bytes(int64_t K, int64_t N, int bits)
+{
+    if (bits < 1 || bits > 8 || K < 0 || N < 0 || (K * bits) % 8 != 0) return 0;
+    return (size_t)N * (size_t)K * (size_t)bits / 8u;
+}
+
+qmm_status qmm_pack(const uint8_t *codes, uint32_t *wq, int64_t K, int64_t N, int bits, qmm_stream stream)
+{
+    qmm_status st = check_shape("qmm_pack", 1, K, N, bits, 32, false);
+    if (st != QMM_OK) return st;
+    if (!codes || !wq) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", "qmm_pack");
+    return hip_status(qmm::launch_pack(codes, wq, (int)K, (int)N, bits, (hipStream_t)stream), "qmm_pack");
+}
+
+qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, int bits, qmm_stream stream)
+{
+    qmm_status st = check_shape("qmm_unpack", 1, K, N, bits, 32, false);
+    if (st != QMM_OK) return st;
+    if (!codes || !wq) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", "qmm_unpack");
+    return hip_status(qmm::launch_unpack(wq, codes, (int)K, (int)N, bits, (hipStream_t)stream), "qmm_unpack");
+}
+
+static qmm_status product(const char *fn, bool gemv, const qmm_half *X, const uint32_t *wq, const qmm_half *s,
+                          const qmm_half *z, qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
+                          qmm_stream stream)
+{
+    qmm_status st = check_shape(fn, M, K, N, bits, G, true);
+    if (st != QMM_OK) return st;
+    if (gemv && M > 16) return fail(QMM_ERR_INVALID_ARG, "%s: M must be <= 16 (use qmm_gemm)", fn);
+    if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    qmm::GemvArgs a{X, wq, s, z, Y, (int)M, (int)K, (int)N, bits, (int)G};
+    hipError_t e = gemv ? qmm::launch_gemv(a, (hipStream_t)stream) : qmm::launch_gemm(a, (hipStream_t)stream);
+    return hip_status(e, fn);
+}
+
+qmm_status qmm_gemv(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z, qmm_half *Y,
+                    int64_t M, int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)
+{
+    return product("qmm_gemv", true, X, wq, s, z, Y, M, K, N, bits, G, stream);
+}
+
+qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z, qmm_half *Y,
+                    int64_t M, int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)
+{
+    return product("qmm_gemm", false, X, wq, s, z, Y, M, K, N, bits, G, stream);
+}
+
+qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
+                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K, int64_t N,
+                         int64_t G, qmm_stream stream)
+{
+    const char *fn = "qmm_gemm_w4a8";
+    qmm_status st = check_shape(fn, M, K, N, 4, G, true);
+    if (st != QMM_OK) return st;
+    if (!Xq || !sx || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (G % 128 != 0 || (G / 128 & (G / 128 - 1)) != 0 || G > 1024)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: G must be 128, 256, 512 or 1024", fn);
+    if ((M + 15) / 16 > 65535) return fail(QMM_ERR_UNSUPPORTED, "%s: M too large", fn);
+    if (acc_out && M * (K / G) * N > (int64_t(1) << 31) - 1)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: accumulator dump too large", fn);
+    qmm::W4A8Args a{Xq, sx, wq, s, z, Y, acc_out, (int)M, (int)K, (int)N, (int)G};
+    return hip_status(qmm::launch_w4a8(a, (hipStream_t)stream), fn);
+}
+
+const char *qmm_status_string(qmm_status status)
+{
+    switch (status) {
+        case QMM_OK: return "ok";
+        case QMM_ERR_INVALID_ARG: return "invalid argument";
+        case QMM_ERR_UNSUPPORTED: return "unsupported shape";
+        case QMM_ERR_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+const char *qmm_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+// gemm.hip -- prefill-shaped product Y[M,N] = X[M,K] . dequant(Wq), any M.
+//
+// f16 MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulation) on weights dequantised
+// in registers: each lane unpacks a whole 32-code run of one column into fp16
+// patterns 1024 + q 2^p and turns them into w' = (q - z) 2^p s with one exact
+// subtraction and one rounding multiply (BitLLM Sec. 2.2, eq. (5), per group).
+// The X tile goes through LDS, double-buffered, already permuted into the
+// run's half-slot order and scaled by 2^-p, so both MFMA operands are plain
+// 16-byte fragments.
+//
+// Workgroup tile 256 (M) x 128 (N), 4 waves as 2 x 2, wave tile 128 x 64 =
+// 8 x 4 MFMA tiles.  K advances 128 rows per step: lane group g (lanes
+// 16g..16g+15) of every MFMA owns run 4t+g.  Workgroups are mapped so that the
+// 8 XCDs each take a contiguous band of M tiles (their X rows stay in that
+// XCD's L2 while the packed weights stream).
+#include "launch.hpp"
+#include "qmm_device.hpp"
+
+namespace qmm {
+
+template <int BITS>
+__device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs)[16])
+{
+    using P = RunPlan<BITS>;
+    _Float16 x[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const half2_t p = as_half2(xr[i]);
+        x[2 * i] = p[0];
+        x[2 * i + 1] = p[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        half2_t v;
+        v[0] = x[P::code[2 * j]];
+        v[1] = x[P::code[2 * j + 1]];
+        if (P::pos[2 * j] | P::pos[2 * j + 1]) {
+            half2_t sc;
+            sc[0] = (_Float16)pow2neg(P::pos[2 * j]);
+            sc[1] = (_Float16)pow2neg(P::pos[2 * j + 1]);
+            v = v * sc;
+        }
+        xs[j] = v;
+    }
+}
+
+constexpr int GEMM_BM = 256, GEMM_BN = 128;
+constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
+constexpr uint32_t GEMM_OOB = 0x80000000u;
+
+template <int BITS, bool PGZ>
+__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+                                                   const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
+                                                   uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
+                                                   int ntiles)
+{
+    using P = RunPlan<BITS>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][GEMM_BM * GEMM_ROWB];
+
+    // XCD-aware tile order: consecutive workgroup ids go round-robin over the 8
+    // XCDs, so give XCD x a contiguous range of tiles (M-major).
+    const int total = mtiles * ntiles;
+    int tile = blockIdx.x;
+    if (total % 8 == 0) tile = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+    const int mt = tile / ntiles, nt = tile % ntiles;
+    const int m0 = mt * GEMM_BM, n0 = nt * GEMM_BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int R = K >> 5, ng = K / G, TT = (R + 3) >> 2;
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
+    const float zdef = (float)(1u << (BITS - 1));
+
+    // X: rows m0.. of the whole K range (OOB rows and runs read zeros).
+    const int mrows = min(GEMM_BM, M - m0);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
+    // Weights, scales, zero-points of this wave's 64 columns.
+    const int wn0 = n0 + wn * 64;
+    const int wcols = max(0, min(64, N - wn0));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)min(wn0, N) * ng, (uint32_t)(wcols * ng * 2));
+    const __amdgpu_buffer_rsrc_t zr =
+        make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
+
+    auto load_x = [&](int tt, uint32_t (&raw)[4][16]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int it = tid + 256 * i;
+            const int row = it >> 2, gg = it & 3;
+            const int run = 4 * tt + gg;
+            const uint32_t off = (run < R) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
+            load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
+        }
+    };
+    auto store_x = [&](int buf, const uint32_t (&raw)[4][16]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int it = tid + 256 * i;
+            const int row = it >> 2, gg = it & 3;
+            half2_t xs[16];
+            x_slots_g<BITS>(raw[i], xs);
+            uint8_t *dst = &lds[buf][row * GEMM_ROWB + gg * 64];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int4_t v;
+                v[0] = (int)as_u32(xs[4 * q + 0]);
+                v[1] = (int)as_u32(xs[4 * q + 1]);
+                v[2] = (int)as_u32(xs[4 * q + 2]);
+                v[3] = (int)as_u32(xs[4 * q + 3]);
+                *reinterpret_cast<int4_t *>(dst + 16 * q) = v;
+            }
+        }
+    };
+    auto load_w = [&](int tt, uint32_t (&d)[4][BITS], uint16_t (&sv)[4], uint16_t (&zv)[4]) {
+        const int run = 4 * tt + g;
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+            const int col = ns * 16 + c;
+            const uint32_t off = (run < R) ? (uint32_t)col * col_bytes + (uint32_t)run * run_bytes : GEMM_OOB;
+            load_dwords<LOAD_STREAM>(wr, off, d[ns], BITS);
+            const uint32_t soff = (run < R) ? (uint32_t)(col * ng + (run * 32) / G) * 2u : GEMM_OOB;
+            sv[ns] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+            zv[ns] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, soff, 0, 0) : (uint16_t)0;
+        }
+    };
+
+    float4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t xraw[4][16];
+    uint32_t dcur[4][BITS], dnext[4][BITS];
+    uint16_t scur[4], snext[4], zcur[4], znext[4];
+    load_x(0, xraw);
+    load_w(0, dcur, scur, zcur);
+    store_x(0, xraw);
+    __syncthreads();
+
+    for (int tt = 0; tt < TT; ++tt) {
+        const int cur = tt & 1;
+        const bool more = tt + 1 < TT;
+        if (more) {
+            load_x(tt + 1, xraw);
+            load_w(tt + 1, dnext, snext, znext);
+        }
+        // dequantise this step's 4 runs (one per N subtile) into B fragments
+        half8_t bq[4][4];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+            uint32_t h[16];
+            run_to_half2<BITS>(dcur[ns], h);
+            half2_t s2;
+            s2[0] = as_half(scur[ns]);
+            s2[1] = s2[0];
+            half2_t z2;
+            z2[0] = as_half(zcur[ns]);
+            z2[1] = z2[0];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * u + e;
+                    half2_t bias;
+                    half2_t p2;
+                    p2[0] = (_Float16)(float)(1u << P::pos[2 * j]);
+                    p2[1] = (_Float16)(float)(1u << P::pos[2 * j + 1]);
+                    if (PGZ) {
+                        half2_t k1;
+                        k1[0] = (_Float16)1024.0f;
+                        k1[1] = (_Float16)1024.0f;
+                        bias = z2 * p2 + k1;
+                    } else {
+                        bias[0] = (_Float16)(1024.0f + zdef * (float)(1u << P::pos[2 * j]));
+                        bias[1] = (_Float16)(1024.0f + zdef * (float)(1u << P::pos[2 * j + 1]));
+                    }
+                    const half2_t w = (as_half2(h[j]) - bias) * s2;
+                    bq[ns][u][2 * e] = w[0];
+                    bq[ns][u][2 * e + 1] = w[1];
+                }
+            }
+        }
+        const uint8_t *abase = &lds[cur][(wm * 128 + c) * GEMM_ROWB + g * 64];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const half8_t a = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ns][u], acc[ms][ns], 0, 0, 0);
+            }
+        }
+        if (more) store_x(cur ^ 1, xraw);
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+#pragma unroll
+                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
+                scur[ns] = snext[ns];
+                zcur[ns] = znext[ns];
+            }
+        }
+    }
+
+    // epilogue: lane (g, c) of MFMA tile (ms, ns) holds rows 4g..4g+3, column c.
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+            const int col = wn0 + ns * 16 + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * 128 + ms * 16 + 4 * g + i;
+                if (row < M && col < N) Y[(size_t)row * N + col] = f32_to_f16_bits(acc[ms][ns][i]);
+            }
+        }
+    }
+}
+
+template <int BITS>
+static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
+{
+    const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + GEMM_BN - 1) / GEMM_BN;
+    const dim3 block(256), grid((unsigned)(mtiles * ntiles));
+    if (a.z)
+        hipLaunchKernelGGL((gemm_kernel<BITS, true>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K, a.N,
+                           a.G, mtiles, ntiles);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BITS, false>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K, a.N,
+                           a.G, mtiles, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)
+{
+    switch (a.bits) {
+        case 1: return gemm_dispatch<1>(a, st);
+        case 2: return gemm_dispatch<2>(a, st);
+        case 3: return gemm_dispatch<3>(a, st);
+        case 4: return gemm_dispatch<4>(a, st);
+        case 5: return gemm_dispatch<5>(a, st);
+        case 6: return gemm_dispatch<6>(a, st);
+        case 7: return gemm_dispatch<7>(a, st);
+        case 8: return gemm_dispatch<8>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qmm

@@ -1,0 +1,35 @@
+// launch.hpp -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+struct GemvArgs {
+    const uint16_t *X;     // fp16 [M][K]
+    const uint32_t *wq;    // [N][K*bits/32]
+    const uint16_t *s;     // fp16 [N][K/G]
+    const uint16_t *z;     // fp16 [N][K/G] or nullptr
+    uint16_t *Y;           // fp16 [M][N]
+    int M, K, N, bits, G;
+};
+
+struct W4A8Args {
+    const int8_t *Xq;      // [M][K]
+    const uint16_t *sx;    // fp16 [M]
+    const uint32_t *wq;    // [N][K/8]
+    const uint16_t *s;     // fp16 [N][K/G]
+    const uint16_t *z;     // fp16 [N][K/G] or nullptr
+    uint16_t *Y;           // fp16 [M][N]
+    int32_t *acc;          // int32 [M][K/G][N] or nullptr
+    int M, K, N, G;
+};
+
+hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, hipStream_t st);
+hipError_t launch_unpack(const uint32_t *wq, uint8_t *codes, int K, int N, int bits, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
+hipError_t launch_gemm(const GemvArgs &a, hipStream_t st);
+hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st);
+
+}  // namespace qmm

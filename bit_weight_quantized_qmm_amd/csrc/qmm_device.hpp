@@ -1,0 +1,84 @@
+// qmm_device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// Packed format: column n of Wq is a little-endian bit stream along K; code i
+// sits at stream bits [i*k, i*k+k).  Because 32 codes of k bits are exactly k
+// dwords, a lane always loads whole "runs" of 32 codes as k dword-aligned
+// dwords and unpacks them in registers (no LDS layout conversion).  This is
+// the register reinterpretation described on the Tilus verdict page
+// (pith.science, arXiv 2504.12984: skeptic critique and referee report on the
+// View instruction, Sec. 3.2 / Fig. 2(c)) written out for each k by hand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+// (a & m) | b as one VALU op (v_and_or_b32).
+__device__ __forceinline__ uint32_t qmm_and_or(uint32_t a, uint32_t m, uint32_t b)
+{
+    return (a & m) | b;
+}
+
+#include "unpack_plan.inc"
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ _Float16 as_half(uint16_t u) { return __builtin_bit_cast(_Float16, u); }
+__device__ __forceinline__ uint16_t as_u16(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// Exact 2^-p as fp16 for 0 <= p <= 10.
+__host__ __device__ constexpr float pow2neg(int p) { return 1.0f / float(1u << p); }
+
+// ---------------------------------------------------------------------------
+// Buffer resources: raw buffer loads carry their own range check (lanes whose
+// byte offset is past num_records read zeros and never fault), which is how
+// ragged column and K tails are handled without divergent branches.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy bits for buffer loads: streamed weights are read once.
+enum : int { LOAD_DEFAULT = 0, LOAD_STREAM = 2 /* nt */ };
+
+template <int AUX>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d, int n)
+{
+    // n is a compile-time constant after inlining; split into x4/x3/x2/x1 pieces.
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+        int4_t v = __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, AUX));
+        d[i] = v[0]; d[i + 1] = v[1]; d[i + 2] = v[2]; d[i + 3] = v[3];
+    }
+    if (n - i == 3) {
+        typedef int int3_t __attribute__((ext_vector_type(3)));
+        int3_t v = __builtin_bit_cast(int3_t, __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * i, 0, AUX));
+        d[i] = v[0]; d[i + 1] = v[1]; d[i + 2] = v[2];
+    } else if (n - i == 2) {
+        typedef int int2_t __attribute__((ext_vector_type(2)));
+        int2_t v = __builtin_bit_cast(int2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i, 0, AUX));
+        d[i] = v[0]; d[i + 1] = v[1];
+    } else if (n - i == 1) {
+        d[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, AUX);
+    }
+}
+
+// fp32 sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// fp32 -> fp16 round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((_Float16)v); }
+
+}  // namespace qmm

@@ -1,0 +1,125 @@
+/*
+ * qmm.h -- C ABI of the k-bit weight-quantized matrix product on AMD MI355X (gfx950).
+ *
+ *     Y[M,N] = X[M,K] . dequant(Wq)[K,N],        w = (q - z) * s
+ *
+ * The operation is the per-group affine dequantisation of BitLLM ("BitLLM:
+ * Efficient Low-Bit, Conversion-Hiding LLM Decoding on Mobile GPUs", Sec. 2.2,
+ * eq. (5) with the integer zero-point of eq. (1) and the per-group granularity
+ * paragraph) applied to unsigned k-bit weight codes, k = 1..8 (the arbitrary
+ * 1-8-bit weight types of the Tilus verdict page, pith.science arXiv
+ * 2504.12984), followed by a product with fp16 activations, or with int8
+ * activations and one scale per token (BitLLM Sec. 4.3 dp4a semantics and
+ * Sec. 4.4 integer accumulation with deferred dequantisation).
+ *
+ * DATA LAYOUT (all row-major, no padding)
+ *   codes  uint8  [K][N]            one code per byte, low k bits used
+ *   Wq     uint32 [N][K*k/32]       column n = one little-endian bit stream along
+ *                                   K: code i at stream bits [i*k, i*k+k), LSB
+ *                                   first; stream bit p = bit (p%32) of dword p/32
+ *                                   of the column.  qmm_packed_bytes() bytes.
+ *   X      fp16   [M][K]            activations (IEEE binary16 bit patterns)
+ *   Xq     int8   [M][K]            int8 activations; sx fp16 [M] per-token scales
+ *   s      fp16   [N][K/G]          scale of (column n, group g); group g = rows
+ *                                   [g*G, (g+1)*G) of K
+ *   z      fp16   [N][K/G] or NULL  zero-point (integer-valued, 0 <= z < 2^k);
+ *                                   NULL means z = 2^(k-1) everywhere
+ *   Y      fp16   [M][N]            output, fp32 accumulation, rounded to nearest even
+ *
+ * OWNERSHIP AND EXECUTION
+ *   Every array pointer is a DEVICE pointer owned by the caller (for example a
+ *   torch tensor's data_ptr()).  The library allocates nothing, keeps no state
+ *   between calls and never synchronises: each call validates its arguments on
+ *   the host, enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *   stream) and returns.  Calls on one stream run in order; calls that write the
+ *   same output from different streams race.
+ *
+ * ERRORS
+ *   Validation runs before any HIP call.  On QMM_ERR_INVALID_ARG or
+ *   QMM_ERR_UNSUPPORTED nothing is enqueued and no output is touched.
+ *   QMM_ERR_HIP reports a failed launch; qmm_last_error() then holds the HIP
+ *   error text (per host thread).  Kernel faults surface at the caller's next
+ *   synchronisation, as usual for HIP.
+ *
+ * COMMON PRECONDITIONS (else QMM_ERR_INVALID_ARG)
+ *   1 <= bits <= 8; K >= 32 and K % 32 == 0 (every column is whole dwords);
+ *   G >= 32, G % 32 == 0 and K % G == 0 (no 32-code run straddles a group);
+ *   N >= 1; M >= 1; required pointers non-NULL.
+ *   Device pointers must be 4-byte aligned (Wq, X, Y: 16-byte aligned is fastest).
+ *   Scales must keep |s| * 2^10 finite in fp16 (|s| < 64) on the MFMA paths.
+ */
+#ifndef QMM_H_
+#define QMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_INVALID_ARG = -1,   /* a precondition failed; nothing was launched */
+    QMM_ERR_UNSUPPORTED = -2,   /* valid arguments beyond an implemented limit; nothing launched */
+    QMM_ERR_HIP = -3            /* a HIP launch failed; see qmm_last_error() */
+} qmm_status;
+
+typedef void *qmm_stream;       /* hipStream_t */
+typedef uint16_t qmm_half;      /* IEEE binary16 bit pattern */
+
+/* Bytes of the packed stream for K x N codes of `bits` bits: N*K*bits/8.
+ * Returns 0 for invalid shapes.  Pure host function. */
+size_t qmm_packed_bytes(int64_t K, int64_t N, int bits);
+
+/* Pack codes [K][N] (low `bits` bits of each byte) into Wq [N][K*bits/32].
+ * Defines the stream format above (contiguous LSB-first packing: BitLLM Sec. 4.3,
+ * Fig. 8(a); the Tilus page's one-bit-string-per-thread reading of View). */
+qmm_status qmm_pack(const uint8_t *codes, uint32_t *wq, int64_t K, int64_t N, int bits,
+                    qmm_stream stream);
+
+/* Test hook: decode Wq back to codes [K][N] with the same in-register unpack
+ * (dword runs -> fp16 bit patterns) that qmm_gemv and qmm_gemm use, then read
+ * each code back out of its fp16 pattern.  Exact inverse of qmm_pack. */
+qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, int bits,
+                      qmm_stream stream);
+
+/* Decode-shaped product, 1 <= M <= 16 (else QMM_ERR_INVALID_ARG):
+ * Y = X . dequant(Wq), fp32 accumulation.  M == 1 runs a split-K VALU kernel
+ * (v_dot2 on fp16 code pairs, per-group scale applied to each 32-code partial
+ * sum); 2 <= M <= 16 runs f16 MFMA with M padded to 16.  Eq. (5) of BitLLM
+ * Sec. 2.2 with per-group s, z. */
+qmm_status qmm_gemv(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
+                    qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
+                    qmm_stream stream);
+
+/* Same arguments and result as qmm_gemv for any M >= 1: f16 MFMA (fp32
+ * accumulation) on weights dequantised in registers, X staged through LDS.
+ * Intended for large M (prefill). */
+qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
+                    qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
+                    qmm_stream stream);
+
+/* Integer-activation product with 4-bit weights (BitLLM Sec. 4.3 dp4a semantics,
+ * Sec. 4.4 deferred dequantisation):
+ *   A[m][g][n] = sum_{i in group g} Xq[m][i] * (q[i][n] - z[n][g])   (exact int32)
+ *   Y[m][n]    = fp16( sx[m] * sum_g s[n][g] * A[m][g][n] )          (fp32)
+ * computed with i8 MFMA.  Xq is symmetric int8 (no activation zero-point; -128
+ * is accepted).  z must be integer-valued in [0, 15] (NULL = 8).  acc_out is
+ * NULL or an int32 [M][K/G][N] array that receives A (for verification).
+ * 1 <= M; QMM_ERR_UNSUPPORTED if M > 16 * 65535. */
+qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
+                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K,
+                         int64_t N, int64_t G, qmm_stream stream);
+
+/* Static text for a status code. */
+const char *qmm_status_string(qmm_status status);
+
+/* Text of the last QMM_ERR_* reported on the calling host thread ("" if none). */
+const char *qmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H_ */

@@ -1,0 +1,125 @@
+"""The C-ABI library without a GPU: it loads, exports what include/qmm.h declares,
+and rejects invalid arguments before any HIP call (so these run on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+LIB = os.path.join(ROOT, "bit_weight_quantized_qmm_amd", "libqmm.so")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import bit_weight_quantized_qmm_amd._build as b
+        b.build()
+    lib = ctypes.CDLL(LIB)
+    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.qmm_packed_bytes.argtypes = [I64, I64, INT]
+    lib.qmm_packed_bytes.restype = ctypes.c_size_t
+    for f in ("qmm_pack", "qmm_unpack"):
+        getattr(lib, f).argtypes = [P, P, I64, I64, INT, P]
+        getattr(lib, f).restype = INT
+    for f in ("qmm_gemv", "qmm_gemm"):
+        getattr(lib, f).argtypes = [P, P, P, P, P, I64, I64, I64, INT, I64, P]
+        getattr(lib, f).restype = INT
+    lib.qmm_gemm_w4a8.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.qmm_gemm_w4a8.restype = INT
+    lib.qmm_status_string.argtypes = [INT]
+    lib.qmm_status_string.restype = ctypes.c_char_p
+    lib.qmm_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("qmm_pack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_binding_lists_every_symbol():
+    import bit_weight_quantized_qmm_amd as q
+    assert sorted(q.SYMBOLS) == declared_symbols()
+
+
+def test_packed_bytes(lib):
+    assert lib.qmm_packed_bytes(4096, 11008, 4) == 4096 * 11008 // 2
+    assert lib.qmm_packed_bytes(8192, 28672, 3) == 8192 * 28672 * 3 // 8
+    assert lib.qmm_packed_bytes(32, 1, 1) == 4
+    assert lib.qmm_packed_bytes(32, 1, 9) == 0
+    assert lib.qmm_packed_bytes(-32, 1, 4) == 0
+
+
+@pytest.mark.parametrize("K,N,bits,expect", [
+    (32, 4, 0, INVALID), (32, 4, 9, INVALID), (48, 4, 4, INVALID), (0, 4, 4, INVALID), (32, 0, 4, INVALID),
+    (1 << 22, 4, 4, UNSUPPORTED),
+])
+def test_pack_validation(lib, K, N, bits, expect):
+    assert lib.qmm_pack(FAKE, FAKE, K, N, bits, None) == expect
+    assert lib.qmm_unpack(FAKE, FAKE, K, N, bits, None) == expect
+    assert lib.qmm_last_error()
+
+
+def test_pack_null_pointers(lib):
+    assert lib.qmm_pack(None, FAKE, 32, 4, 4, None) == INVALID
+    assert lib.qmm_unpack(FAKE, None, 32, 4, 4, None) == INVALID
+
+
+@pytest.mark.parametrize("M,K,N,bits,G,expect", [
+    (1, 4096, 8, 0, 128, INVALID),
+    (1, 4096, 8, 9, 128, INVALID),
+    (1, 4016, 8, 4, 16 * 2, INVALID),   # K % 32
+    (1, 4096, 8, 4, 48, INVALID),       # G % 32
+    (1, 4096, 8, 4, 16, INVALID),       # G < 32
+    (1, 4096, 8, 4, 384, INVALID),      # K % G
+    (0, 4096, 8, 4, 128, INVALID),
+    (1, 4096, 0, 4, 128, INVALID),
+    (1, 1 << 22, 8, 4, 128, UNSUPPORTED),
+])
+def test_product_validation(lib, M, K, N, bits, G, expect):
+    for fn in (lib.qmm_gemv, lib.qmm_gemm):
+        assert fn(FAKE, FAKE, FAKE, None, FAKE, M, K, N, bits, G, None) == expect
+
+
+def test_gemv_rejects_large_m(lib):
+    assert lib.qmm_gemv(FAKE, FAKE, FAKE, None, FAKE, 17, 4096, 8, 4, 128, None) == INVALID
+
+
+def test_product_null_pointers(lib):
+    for fn in (lib.qmm_gemv, lib.qmm_gemm):
+        assert fn(None, FAKE, FAKE, None, FAKE, 1, 256, 8, 4, 64, None) == INVALID
+        assert fn(FAKE, None, FAKE, None, FAKE, 1, 256, 8, 4, 64, None) == INVALID
+        assert fn(FAKE, FAKE, None, None, FAKE, 1, 256, 8, 4, 64, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, None, None, 1, 256, 8, 4, 64, None) == INVALID
+
+
+def test_w4a8_validation(lib):
+    f = lib.qmm_gemm_w4a8
+    assert f(None, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 128, None) == INVALID
+    assert f(FAKE, None, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 128, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 100, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 64, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 384, None) in (INVALID, UNSUPPORTED)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, 4096, 64, 128, None) == INVALID
+
+
+def test_status_strings(lib):
+    assert lib.qmm_status_string(OK) == b"ok"
+    for st in (INVALID, UNSUPPORTED, HIPERR):
+        assert lib.qmm_status_string(st) and lib.qmm_status_string(st) != b"ok"

@@ -1,0 +1,278 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+* packed streams and unpacked codes: bit-exact;
+* fp16 products: max|Y_gpu - Y_ref| / max|Y_ref| <= 4e-3, Y_ref the oracle's
+  unrounded fp64 result; exactly zero when every code equals its zero-point;
+* int8-activation product: the int32 per-group sums bit-exact, Y within 4e-3.
+Small shapes cover several tiles, ragged tails and every k; the full
+workload shapes are checked on outputs the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+TOL = 4e-3
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_weight_quantized_qmm_amd as qmm
+    return qmm
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\nCASE {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def stream_bytes(wq):
+    return wq.cpu().numpy().view(np.uint8).reshape(wq.shape[0], -1)
+
+
+def rel_err(y_gpu, y_ref):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    den = np.abs(y_ref).max()
+    return np.abs(y - y_ref).max() / den
+
+
+def gpu_pack(q, codes, bits):
+    return q.pack(dev(codes), bits)
+
+
+def guarded(shape, dtype, guard=256):
+    """Output tensor followed by a guard region filled with a canary pattern."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + guard,), 0x5A if dtype == torch.uint8 else -7, dtype=dtype, device=DEV)
+    return buf, buf[:n].view(*shape)
+
+
+def guard_intact(buf, n):
+    tail = buf[n:].cpu()
+    return bool((tail == tail[0]).all()) and int(tail[0]) in (0x5A, -7)
+
+
+# ------------------------------------------------------------- pack/unpack --
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("K,N", [(32, 1), (96, 37), (256, 256), (4096, 300)])
+def test_pack_unpack_bit_exact(q, orc, bits, K, N):
+    c = synthetic.make_case(1, K, N, bits, 32, synthetic.seed_for(90, bits, K + N))
+    wq = gpu_pack(q, c["codes"], bits)
+    assert np.array_equal(stream_bytes(wq), orc.pack(c["codes"], bits))
+    buf, out = guarded((K, N), torch.uint8)
+    q.unpack(wq, K, N, bits, out=out)
+    assert np.array_equal(out.cpu().numpy(), orc.unpack(orc.pack(c["codes"], bits), K, N, bits))
+    assert guard_intact(buf, K * N)
+
+
+def test_pack_masks_wide_codes(q, orc):
+    g = synthetic.rng(5)
+    wide = g.integers(0, 256, size=(128, 40), dtype=np.uint8)
+    for bits in range(1, 8):
+        assert np.array_equal(stream_bytes(gpu_pack(q, wide, bits)), orc.pack(wide, bits))
+
+
+# ------------------------------------------------------------ fp16 products --
+def run_product(q, fn, c):
+    wq = gpu_pack(q, c["codes"], c["bits"])
+    z = None if c["z"] is None else dev(c["z"])
+    return fn(dev(c["X"]), wq, dev(c["s"]), z, c["bits"], c["G"])
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("pgz", [False, True])
+def test_gemv_small(q, orc, bits, M, pgz):
+    for (K, N, G) in ((256, 40, 64), (96, 19, 32), (1024, 130, 128)):
+        c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(91, bits, M + K + N), per_group_z=pgz)
+        Y = run_product(q, q.gemv, c)
+        ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+        assert rel_err(Y, ref) <= TOL, (K, N, G)
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_gemv_m1_long_k(q, orc, bits):
+    """K beyond the single-wave M = 1 kernel's register slice: the MFMA path with several K passes."""
+    c = synthetic.make_case(1, 32768, 24, bits, 128, synthetic.seed_for(92, bits), per_group_z=True)
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, 128)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("M", [1, 7, 257])
+def test_gemm_small(q, orc, bits, M):
+    for (K, N, G, pgz) in ((384, 200, 128, False), (96, 37, 32, True), (512, 130, 64, True)):
+        c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(93, bits, M + K), per_group_z=pgz)
+        Y = run_product(q, q.gemm, c)
+        ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+        assert rel_err(Y, ref) <= TOL, (K, N, G, pgz)
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+@pytest.mark.parametrize("bits", [1, 3, 4, 8])
+def test_codes_equal_zero_point_give_exact_zero(q, fn, bits):
+    K, N, G, M = 512, 70, 128, 5
+    g = synthetic.rng(99 + bits)
+    z = synthetic.zeros_uniform(g, bits, N, K // G)
+    codes = np.repeat(z.astype(np.uint8).T, G, axis=0)
+    c = dict(bits=bits, G=G, X=synthetic.fp16_normal(g, (M, K)), codes=codes,
+             s=synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G)), z=z)
+    Y = run_product(q, getattr(q, fn), c)
+    assert not Y.float().abs().max().item()
+    mid = dict(c, codes=np.full((K, N), 1 << (bits - 1), dtype=np.uint8), z=None)
+    Y = run_product(q, getattr(q, fn), mid)
+    assert not Y.float().abs().max().item()
+
+
+def test_deterministic(q):
+    c = synthetic.make_case(16, 2048, 300, 5, 128, 7, per_group_z=True)
+    wq = gpu_pack(q, c["codes"], 5)
+    args = (dev(c["X"]), wq, dev(c["s"]), dev(c["z"]), 5, 128)
+    for fn in (q.gemv, q.gemm):
+        outs = [fn(*args).cpu() for _ in range(3)]
+        assert all(torch.equal(outs[0], o) for o in outs[1:])
+    x1 = dev(c["X"][:1])
+    outs = [q.gemv(x1, *args[1:]).cpu() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_outputs_stay_in_bounds(q):
+    c = synthetic.make_case(3, 256, 45, 4, 64, 8)
+    wq = gpu_pack(q, c["codes"], 4)
+    for fn in (q.gemv, q.gemm):
+        buf, out = guarded((3, 45), torch.float16)
+        fn(dev(c["X"]), wq, dev(c["s"]), None, 4, 64, out=out)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, 3 * 45)
+
+
+def test_invalid_arguments_raise(q):
+    c = synthetic.make_case(17, 256, 16, 4, 64, 9)
+    wq = gpu_pack(q, c["codes"], 4)
+    with pytest.raises(q.QmmError):
+        q.gemv(dev(c["X"]), wq, dev(c["s"]), None, 4, 64)          # M = 17 > 16
+
+
+# ---------------------------------------------------------- full workloads --
+def sampled_check(orc, Y, c, count=3000, seed=0, st=None):
+    g = synthetic.rng(seed)
+    M, N = Y.shape
+    ms = g.integers(0, M, size=count)
+    ns = g.integers(0, N, size=count)
+    ms[:4] = [0, M - 1, 0, M - 1]
+    ns[:4] = [0, N - 1, N - 1, 0]
+    st = orc.pack(c["codes"], c["bits"]) if st is None else st
+    ref = orc.qmm_sampled(c["X"], st, c["s"], c["z"], c["bits"], c["G"], ms, ns)
+    y = Y.float().cpu().numpy()[ms, ns].astype(np.float64)
+    return np.abs(y - ref).max() / np.abs(ref).max()
+
+
+def test_tiny_workload(q, orc):
+    w = synthetic.TINY
+    c = synthetic.make_case(1, w["K"], w["N"], 4, w["G"], synthetic.seed_for(1, 4), s_range=w["s_range"])
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], 4), c["s"], None, 4, w["G"])
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", synthetic.DECODE_7B["bits"])
+def test_decode_7b_workload(q, orc, bits):
+    w = synthetic.DECODE_7B
+    c = synthetic.make_case(1, w["K"], w["N"], bits, w["G"], synthetic.seed_for(2, bits), s_range=w["s_range"])
+    wq = gpu_pack(q, c["codes"], bits)
+    st = orc.pack(c["codes"], bits)
+    assert np.array_equal(stream_bytes(wq), st)
+    assert np.array_equal(q.unpack(wq, w["K"], w["N"], bits).cpu().numpy(), orc.unpack(st, w["K"], w["N"], bits))
+    Y = q.gemv(dev(c["X"]), wq, dev(c["s"]), None, bits, w["G"])
+    ref = orc.qmm(c["X"], st, c["s"], None, bits, w["G"])
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", synthetic.BATCHED_70B["bits"])
+def test_batched_70b_workload(q, orc, bits):
+    w = synthetic.BATCHED_70B
+    c = synthetic.make_case(16, w["K"], w["N"], bits, w["G"], synthetic.seed_for(3, bits), per_group_z=True,
+                            s_range=w["s_range"])
+    wq = gpu_pack(q, c["codes"], bits)
+    st = orc.pack(c["codes"], bits)
+    assert np.array_equal(stream_bytes(wq), st)
+    assert np.array_equal(q.unpack(wq, w["K"], w["N"], bits).cpu().numpy(), c["codes"])
+    s, z = dev(c["s"]), dev(c["z"])
+    for M in w["Ms"]:
+        cm = dict(c, X=c["X"][:M])
+        Y = q.gemv(dev(cm["X"]), wq, s, z, bits, w["G"])
+        assert sampled_check(orc, Y, cm, seed=M, st=st) <= TOL, M
+
+
+def test_prefill_workload(q, orc):
+    w = synthetic.PREFILL
+    c = synthetic.make_case(w["M"], w["K"], w["N"], 4, w["G"], synthetic.seed_for(4, 4), s_range=w["s_range"])
+    Y = run_product(q, q.gemm, c)
+    assert sampled_check(orc, Y, c, count=4000) <= TOL
+
+
+# ------------------------------------------------------------------ W4A8 ---
+def run_w4a8(q, c, with_acc=True):
+    wq = gpu_pack(q, c["codes"], 4)
+    M, K = c["Xq"].shape
+    N = c["codes"].shape[1]
+    acc = torch.full((M, K // c["G"], N), -12345, dtype=torch.int32, device=DEV) if with_acc else None
+    z = None if c["z"] is None else dev(c["z"])
+    Y = q.gemm_w4a8(dev(c["Xq"]), dev(c["sx"]), wq, dev(c["s"]), z, c["G"], acc_out=acc)
+    return Y, acc
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33])
+@pytest.mark.parametrize("G,pgz", [(128, False), (128, True), (256, True)])
+def test_w4a8_small(q, orc, M, G, pgz):
+    K, N = 1024, 70
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(95, M, G), per_group_z=pgz)
+    Y, acc = run_w4a8(q, c)
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], c["z"], G)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
+
+
+def test_w4a8_extreme_activations(q, orc):
+    """-128 everywhere and codes at the ends of their range: int32 sums still exact."""
+    M, K, N, G = 16, 512, 40, 128
+    c = synthetic.make_w4a8_case(M, K, N, G, 11, per_group_z=True)
+    c["Xq"][:] = -128
+    c["codes"][:, ::2] = 15
+    Y, acc = run_w4a8(q, c)
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], c["z"], G)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
+
+
+def test_w4a8_workload(q, orc):
+    w = synthetic.W4A8_8B
+    c = synthetic.make_w4a8_case(w["M"], w["K"], w["N"], w["G"], synthetic.seed_for(5, 4))
+    Y, acc = run_w4a8(q, c)
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], None, w["G"])
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
+    Y2, _ = run_w4a8(q, c, with_acc=False)
+    assert torch.equal(Y.cpu(), Y2.cpu())
