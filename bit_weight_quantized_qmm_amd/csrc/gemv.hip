@@ -285,6 +285,176 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------------------
+// 1 <= M <= 4 (the decode shapes): f16 MFMA with one accumulator row per
+// (activation row m, run e).  A workgroup of ks waves owns one 16-column tile;
+// the waves split K, T steps of 128 rows each.  In a step, lane group g holds
+// run 4t+g of column lane%16 as fp16 patterns (the B operand, straight from
+// run_to_half2); the A operand row 4m+e carries x_m (slot order, scaled by
+// 2^-p) only in lane group e, zeros elsewhere, so accumulator row 4m+e is the
+// partial sum of run 4t+e alone.  Starting the accumulator at minus the run's
+// bias sum leaves sum x*(q - z) per run; y += s * that, with the run's own
+// group scale, so any G works.  X is staged once per workgroup in LDS (slot
+// order + per-run bias sums); the tile's scales too.  Weight loads are issued
+// right after the X and scale loads, before any arithmetic.
+// ---------------------------------------------------------------------------
+template <int BITS, int T, int IPT, bool G128, bool PGZ>
+__global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restrict__ X,
+                                                         const uint32_t *__restrict__ wq,
+                                                         const uint16_t *__restrict__ s,
+                                                         const uint16_t *__restrict__ z, uint16_t *__restrict__ Y,
+                                                         int M, int K, int N, int G, int ks)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using P = RunPlan<BITS>;
+    const int R = K >> 5, R4 = (R + 3) & ~3, TT = R4 >> 2, ng = K / G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = 64 * ks;
+    const int g = lane >> 4, c = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int nvalid = min(16, N - n0);
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
+
+    // LDS: xs [M][R4] runs x 64 B | 64 B zeros | 64 B dummy | c1 [M][R4] + 4 dummy |
+    //      c2 [M][R4] + 4 dummy (PGZ) | sl [16][ng] + 8 dummy | zl [16][ng] + 8 dummy (PGZ) |
+    //      red [ks][4][16].  Staging threads without an item write the dummy slots, so the
+    //      staging code has no branches (a branch would let the compiler sink the
+    //      activation loads behind the weight loads, and loads complete in order).
+    const uint32_t xs_bytes = (uint32_t)M * R4 * 64u;
+    const int MR = M * R4 + 4;
+    float *c1 = reinterpret_cast<float *>(smem + xs_bytes + 128);
+    float *c2 = c1 + MR;
+    uint16_t *sl = reinterpret_cast<uint16_t *>(c2 + (PGZ ? MR : 0));
+    uint16_t *zl = sl + 16 * ng + 8;
+    float *red = reinterpret_cast<float *>(smem + ((xs_bytes + 128 + 4u * MR * (PGZ ? 2 : 1) +
+                                                    2u * (16 * ng + 8) * (PGZ ? 2 : 1) + 15u) & ~15u));
+
+    // 1. activations for the staging (IPT (row, run) items per thread)
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
+    uint32_t raw[IPT][16];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it = tid + i * nthreads;
+        const int m = it / R4, r = it - m * R4;
+        const uint32_t off = (m < M && r < R) ? ((uint32_t)m * K + (uint32_t)r * 32u) * 2u : OOB;
+        load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
+    }
+    // 2. the tile's scales (and zero-points): 16 contiguous rows of ng halves
+    const uint32_t sbytes = (uint32_t)nvalid * ng * 2u;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)n0 * ng, sbytes);
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z + (size_t)n0 * ng : s, PGZ ? sbytes : 0u);
+    uint32_t sraw[4], zraw[4];
+    const bool s_thread = tid < 2 * ng;   // 16 * ng halves = 2 * ng chunks of 16 B
+    load_dwords<LOAD_DEFAULT>(sr, s_thread ? (uint32_t)tid * 16u : OOB, sraw, 4);
+    if (PGZ) load_dwords<LOAD_DEFAULT>(zr, s_thread ? (uint32_t)tid * 16u : OOB, zraw, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. this wave's packed weights, all in flight before any arithmetic
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)n0 * R * BITS, (uint32_t)nvalid * col_bytes);
+    const int tt0 = wave * T;
+    uint32_t d[T][BITS];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int run = 4 * (tt0 + t) + g;
+        const uint32_t off = (run < R) ? (uint32_t)c * col_bytes + (uint32_t)run * run_bytes : OOB;
+        load_dwords<LOAD_STREAM>(wr, off, d[t], BITS);
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. stage X in slot order with its per-run bias sums; scales; zero pad
+    const float zdef = (float)(1u << (BITS - 1));
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it0 = tid + i * nthreads;
+        const int it = it0 < M * R4 ? it0 : M * R4;   // M * R4 = the dummy item
+        {
+            half2_t xs[16];
+            x_slots<BITS>(raw[i], xs);
+            float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                if (PGZ) {
+                    half2_t k1;
+                    k1[0] = (_Float16)1024.0f;
+                    k1[1] = (_Float16)1024.0f;
+                    a1 = __builtin_amdgcn_fdot2(xs[p], k1, a1, false);
+                    a2 = __builtin_amdgcn_fdot2(xs[p], slot_pow2<BITS>(p), a2, false);
+                } else {
+                    a1 = __builtin_amdgcn_fdot2(xs[p], slot_bias<BITS>(p, zdef), a1, false);
+                }
+            }
+            int4_t *dst = reinterpret_cast<int4_t *>(smem + (it0 < M * R4 ? (uint32_t)it * 64u : xs_bytes + 64u));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dst[q] = int4_t{(int)as_u32(xs[4 * q]), (int)as_u32(xs[4 * q + 1]), (int)as_u32(xs[4 * q + 2]),
+                                (int)as_u32(xs[4 * q + 3])};
+            c1[it] = a1;
+            if (PGZ) c2[it] = a2;
+        }
+    }
+    {
+        const int si = s_thread ? 8 * tid : 16 * ng;   // 16 * ng = the dummy chunk
+        *reinterpret_cast<int4_t *>(sl + si) = int4_t{(int)sraw[0], (int)sraw[1], (int)sraw[2], (int)sraw[3]};
+        if (PGZ)
+            *reinterpret_cast<int4_t *>(zl + si) = int4_t{(int)zraw[0], (int)zraw[1], (int)zraw[2], (int)zraw[3]};
+    }
+    if (tid < 4) reinterpret_cast<int4_t *>(smem + xs_bytes)[tid] = int4_t{0, 0, 0, 0};
+    __syncthreads();
+
+    // 5. K steps: 4 MFMAs per step, bias as the accumulator's start value
+    const int r_row = c;                          // MFMA A row held by this lane
+    const int am = r_row >> 2, ae = r_row & 3;    // (activation row, run) of that A row
+    const bool a_live = (ae == g) && (am < M);
+    const int om = g;                             // output rows 4g..4g+3 = (row g, runs 0..3)
+    const int omc = min(om, M - 1);
+    float y = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int tt = tt0 + t;
+        if (tt >= TT) break;                       // wave-uniform
+        uint32_t h[16];
+        run_to_half2<BITS>(d[t], h);
+        const float4_t cb = *reinterpret_cast<const float4_t *>(c1 + omc * R4 + 4 * tt);
+        float4_t acc;
+        if (PGZ) {
+            const float4_t cz = *reinterpret_cast<const float4_t *>(c2 + omc * R4 + 4 * tt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gi = min(((4 * tt + e) * 32) / G, ng - 1);
+                acc[e] = -fmaf((float)as_half(zl[c * ng + gi]), cz[e], cb[e]);
+            }
+        } else {
+            acc = -cb;
+        }
+        const uint32_t abase = a_live ? ((uint32_t)(am * R4 + 4 * tt + g) * 64u) : xs_bytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const half8_t a = *reinterpret_cast<const half8_t *>(smem + abase + 16u * u);
+            const half8_t b = __builtin_bit_cast(half8_t, int4_t{(int)h[4 * u], (int)h[4 * u + 1],
+                                                                 (int)h[4 * u + 2], (int)h[4 * u + 3]});
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        }
+        if (G128) {
+            const float sc = (float)as_half(sl[c * ng + (tt * 128) / G]);
+            y = fmaf(sc, (acc[0] + acc[1]) + (acc[2] + acc[3]), y);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gi = min(((4 * tt + e) * 32) / G, ng - 1);
+                y = fmaf((float)as_half(sl[c * ng + gi]), acc[e], y);
+            }
+        }
+    }
+
+    // 6. fixed-order sum over the ks waves
+    if (om < M) red[(wave * 4 + om) * 16 + c] = y;
+    __syncthreads();
+    if (tid < M * 16) {
+        const int m = tid >> 4, cc = tid & 15;
+        float v = 0.f;
+        for (int w = 0; w < ks; ++w) v += red[(w * 4 + m) * 16 + cc];
+        if (cc < nvalid) Y[(size_t)m * N + n0 + cc] = f32_to_f16_bits(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch selection.
 // ---------------------------------------------------------------------------
 template <int BITS, bool PGZ>
@@ -331,15 +501,68 @@ static hipError_t gemv_mfma_launch(const GemvArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// LDS bytes of gemv_rows_kernel for (M, K, G, ks); 0 if it does not apply.
+static size_t rows_lds_bytes(int M, int K, int G, int ks, bool pgz)
+{
+    const int R = K / 32, R4 = (R + 3) & ~3, ng = K / G;
+    size_t b = (size_t)M * R4 * 64 + 128 + 4u * (size_t)(M * R4 + 4) * (pgz ? 2 : 1) +
+               2u * (size_t)(16 * ng + 8) * (pgz ? 2 : 1);
+    b = (b + 15) & ~(size_t)15;
+    return b + (size_t)ks * 4 * 16 * 4;
+}
+
+template <int BITS, int T, int IPT, bool G128, bool PGZ>
+static hipError_t gemv_rows_go(const GemvArgs &a, int ks, size_t lds, hipStream_t st)
+{
+    static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
+    if (!attr_set) {
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, T, IPT, G128, PGZ>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const dim3 block(64 * ks), grid((a.N + 15) / 16);
+    hipLaunchKernelGGL((gemv_rows_kernel<BITS, T, IPT, G128, PGZ>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y,
+                       a.M, a.K, a.N, a.G, ks);
+    return hipGetLastError();
+}
+
+template <int BITS, int IPT, bool G128, bool PGZ>
+static hipError_t gemv_rows_pick_t(const GemvArgs &a, int T, int ks, size_t lds, hipStream_t st)
+{
+    switch (T) {
+        case 1: return gemv_rows_go<BITS, 1, IPT, G128, PGZ>(a, ks, lds, st);
+        case 2: return gemv_rows_go<BITS, 2, IPT, G128, PGZ>(a, ks, lds, st);
+        case 4: return gemv_rows_go<BITS, 4, IPT, G128, PGZ>(a, ks, lds, st);
+        default: return gemv_rows_go<BITS, 8, IPT, G128, PGZ>(a, ks, lds, st);
+    }
+}
+
+template <int BITS, int IPT>
+static hipError_t gemv_rows_pick(const GemvArgs &a, int T, int ks, size_t lds, hipStream_t st)
+{
+    const bool g128 = a.G % 128 == 0;
+    if (a.z) return g128 ? gemv_rows_pick_t<BITS, IPT, true, true>(a, T, ks, lds, st)
+                         : gemv_rows_pick_t<BITS, IPT, false, true>(a, T, ks, lds, st);
+    return g128 ? gemv_rows_pick_t<BITS, IPT, true, false>(a, T, ks, lds, st)
+                : gemv_rows_pick_t<BITS, IPT, false, false>(a, T, ks, lds, st);
+}
+
 template <int BITS>
 static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
 {
-    const int R = a.K / 32;
-    const int rpl_need = (R + 63) / 64;
-    if (a.M == 1 && rpl_need <= 8) {
-        int rpl = 1;
-        while (rpl < rpl_need) rpl <<= 1;
-        return a.z ? gemv_m1_launch<BITS, true>(a, rpl, st) : gemv_m1_launch<BITS, false>(a, rpl, st);
+    const int R = a.K / 32, TT = (R + 3) / 4;
+    if (a.M <= 4) {
+        int T = 1;
+        while (T < 8 && T < TT) T <<= 1;
+        const int ks = (TT + T - 1) / T;
+        const size_t lds = rows_lds_bytes(a.M, a.K, a.G, ks, a.z != nullptr);
+        const int R4 = (R + 3) & ~3;
+        if (ks <= 16 && lds <= 160 * 1024 && 2 * (a.K / a.G) <= 64 * ks) {
+            if (a.M * R4 <= 64 * ks) return gemv_rows_pick<BITS, 1>(a, T, ks, lds, st);
+            if (a.M * R4 <= 2 * 64 * ks) return gemv_rows_pick<BITS, 2>(a, T, ks, lds, st);
+        }
     }
     return a.z ? gemv_mfma_launch<BITS, true>(a, st) : gemv_mfma_launch<BITS, false>(a, st);
 }

@@ -19,10 +19,14 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 
-// (a & m) | b as one VALU op (v_and_or_b32).
+// (a & m) | b as one VALU op.  Written out because with two literal constants
+// the compiler otherwise emits v_and_b32 + v_or_b32; here the mask goes in an
+// SGPR and the OR operand in a VGPR (one constant-bus read, as VOP3 allows).
 __device__ __forceinline__ uint32_t qmm_and_or(uint32_t a, uint32_t m, uint32_t b)
 {
-    return (a & m) | b;
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(b));
+    return r;
 }
 
 #include "unpack_plan.inc"
