@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     const int mt = tile / ntiles, nt = tile % ntiles;
     const int m0 = mt * GEMM_BM, n0 = nt * GEMM_BN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int wm = wave & 1, wn = wave >> 1;
     const int R = K >> 5, ng = K / G, TT = (R + 3) >> 2;

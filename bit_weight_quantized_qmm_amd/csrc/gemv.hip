@@ -5,6 +5,8 @@
 // dword-aligned runs (qmm_device.hpp) into fp16 patterns 1024 + q * 2^p; the
 // matching activation is pre-scaled by 2^-p, so a dot product with the pattern
 // gives sum x*q plus a code-independent bias that is removed once per run.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -65,103 +67,180 @@ __device__ __forceinline__ half2_t slot_pow2(int j)
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every resource we build
 
 // ---------------------------------------------------------------------------
-// M = 1: split-K across the 64 lanes of a wave.  A wave owns CPW consecutive
-// columns; lane l owns runs l, l+64, ... (RPL of them) of every column, keeps
-// the matching activations in VGPRs, and issues all its weight loads before
-// any arithmetic.  Per run: 16 v_dot2_f32_f16 give a = sum x'(1024 + q 2^p);
-// y += s_g * (a - bias) with bias = sum x'(1024 + z 2^p) (precomputed per lane
-// for a fixed z, or c1 + z * c2 for per-group z).  A wave reduction finishes
-// each column.
+// M = 1: split-K across the 64 lanes of a wave, one 32-code run per lane and
+// load, so a wave's load of one column is one contiguous k*256-byte stretch
+// (the access pattern of a plain streaming read).  A workgroup of 4 waves owns
+// 4*CPW consecutive columns.  Once per workgroup, X is staged in LDS in the
+// unpack's slot order (scaled by 2^-p) with per-run bias sums, and the
+// columns' scales too; the activation and scale loads go out before the
+// weight loads, so the staging overlaps the weight stream.  Lane l owns runs
+// l, l+64, ... (RPL of them); per run 16 v_dot2_f32_f16 give
+// a = sum x'(1024 + q 2^p), and y += s_g * (a - bias).  A DPP reduction
+// finishes each column.
 // ---------------------------------------------------------------------------
-template <int BITS, int RPL, int CPW, bool PGZ>
+template <int CTRL, int ROWM, int BANKM, bool BC>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWM, BANKM, BC);
+    return v + __builtin_bit_cast(float, s);
+}
+
+// Sum over the 64 lanes of a wave; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    v = dpp_add<0xB1, 0xF, 0xF, true>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF, 0xF, true>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF, 0xF, true>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF, 0xF, true>(v);   // row_mirror: every lane holds its row's sum
+    v = dpp_add<0x142, 0xA, 0xF, false>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC, 0xF, false>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+template <int BITS, int RPL, int D, int IPT, bool PGZ>
 __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                       const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                       uint16_t *__restrict__ Y, int K, int N, int G)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-    const int n0 = wave * CPW;
-    if (n0 >= N) return;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int R = K >> 5, ng = K / G;
-    const uint32_t run_bytes = 4u * BITS;
-    const uint32_t col_bytes = (uint32_t)R * run_bytes;
-    const int ncols = min(CPW, N - n0);
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
+    // waves sweep the columns together: wave w takes w, w + W, w + 2W, ...
+    const int W = (int)gridDim.x * 4;
+    const int w = (int)blockIdx.x * 4 + wave;
+    const int ncw = w < N ? (N - 1 - w) / W + 1 : 0;    // columns of this wave (<= 64)
 
-    // 1. every weight load of this wave in flight first (OOB lanes read zeros).
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)n0 * R * BITS, (uint32_t)ncols * col_bytes);
-    uint32_t d[CPW][RPL][BITS];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            const int r = lane + 64 * j;
-            const uint32_t off = (r < R) ? (uint32_t)c * col_bytes + (uint32_t)r * run_bytes : OOB;
-            load_dwords<LOAD_STREAM>(wr, off, d[c][j], BITS);
-        }
+    // LDS: xs [R] runs x 64 B | 64 B zeros | 64 B dummy | c1 [R] + 4 | c2 [R] + 4 (PGZ)
+    const uint32_t xs_bytes = (uint32_t)R * 64u;
+    float *c1 = reinterpret_cast<float *>(smem + xs_bytes + 128);
+    float *c2 = c1 + R + 4;
 
-    // 2. scale (and zero-point) of each (column, run).
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)n0 * ng, (uint32_t)(ncols * ng * 2));
-    const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z + (size_t)n0 * ng : s, PGZ ? (uint32_t)(ncols * ng * 2) : 0u);
-    uint16_t sv[CPW][RPL], zv[CPW][RPL];
+    // 1. activations for the staging (IPT runs per thread)
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)K * 2u);
+    uint32_t raw[IPT][16];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it = tid + 256 * i;
+        load_dwords<LOAD_DEFAULT>(xr, it < R ? (uint32_t)it * 64u : OOB, raw[i], 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. prefetch the first D columns (weights and per-run scales)
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)min((size_t)N * col_bytes, (size_t)0x7fffffffu));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint32_t)(N * ng * 2));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
+    // Branch-free addressing: a column past N lies past the end of the resource
+    // (the load returns zeros), and a run past K reads some other column's bits
+    // but meets a zero activation and a zero bias, so it adds nothing.
+    int gi[RPL];
+    uint32_t roff[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int r = lane + 64 * j;
-        const int gi = (r * 32) / G;
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const uint32_t off = (r < R) ? (uint32_t)(c * ng + gi) * 2u : OOB;
-            sv[c][j] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-            zv[c][j] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : (uint16_t)0;
-        }
+        gi[j] = min((r * 32) / G, ng - 1);
+        roff[j] = (uint32_t)r * run_bytes;
     }
+    uint32_t d[D][RPL][BITS];
+    uint16_t sv[D][RPL], zv[D][RPL];
+    auto issue = [&](int slot, int i) {
+        const uint32_t n = (uint32_t)(w + i * W);
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            load_dwords<LOAD_STREAM>(wr, n * col_bytes + roff[j], d[slot][j], BITS);
+            const uint32_t so = (n * (uint32_t)ng + (uint32_t)gi[j]) * 2u;
+            sv[slot][j] = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
+            zv[slot][j] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, so, 0, 0) : (uint16_t)0;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep slots in issue order (loads complete in order)
+    };
+#pragma unroll
+    for (int q = 0; q < D; ++q) issue(q, q);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 3. this lane's activations, in slot order, and their bias sums.
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)K * 2u);
-    half2_t xs[RPL][16];
-    float c1[RPL], c2[RPL];
+    // 3. staging: waves that own items convert X to slot order with bias sums
     const float zdef = (float)(1u << (BITS - 1));
 #pragma unroll
+    for (int i = 0; i < IPT; ++i) asm volatile("" ::"v"(raw[i][0]), "v"(raw[i][15]));   // keep the loads here
+    if (tid < 4) reinterpret_cast<int4_t *>(smem + xs_bytes)[tid] = int4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (256 * i + 64 * wave < R) {               // wave-uniform
+            const int it0 = tid + 256 * i;
+            const int it = it0 < R ? it0 : R;        // R = the dummy item
+            half2_t xs[16];
+            x_slots<BITS>(raw[i], xs);
+            float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                if (PGZ) {
+                    half2_t k1;
+                    k1[0] = (_Float16)1024.0f;
+                    k1[1] = (_Float16)1024.0f;
+                    a1 = __builtin_amdgcn_fdot2(xs[p], k1, a1, false);
+                    a2 = __builtin_amdgcn_fdot2(xs[p], slot_pow2<BITS>(p), a2, false);
+                } else {
+                    a1 = __builtin_amdgcn_fdot2(xs[p], slot_bias<BITS>(p, zdef), a1, false);
+                }
+            }
+            int4_t *dst = reinterpret_cast<int4_t *>(smem + (it0 < R ? (uint32_t)it * 64u : xs_bytes + 64u));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dst[q] = int4_t{(int)as_u32(xs[4 * q]), (int)as_u32(xs[4 * q + 1]), (int)as_u32(xs[4 * q + 2]),
+                                (int)as_u32(xs[4 * q + 3])};
+            c1[it] = a1;
+            if (PGZ) c2[it] = a2;
+        }
+    }
+    __syncthreads();
+
+    // 4. this lane's activations and bias sums (runs past K read the zero slot)
+    half2_t xv[RPL][16];
+    float b1[RPL], b2[RPL];
+#pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int r = lane + 64 * j;
-        uint32_t raw[16];
-        load_dwords<LOAD_DEFAULT>(xr, (r < R) ? (uint32_t)r * 64u : OOB, raw, 16);
-        x_slots<BITS>(raw, xs[j]);
-        float a1 = 0.f, a2 = 0.f;
+        const int4_t *src = reinterpret_cast<const int4_t *>(smem + (r < R ? (uint32_t)r * 64u : xs_bytes));
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            if (PGZ) {
-                half2_t k1;
-                k1[0] = (_Float16)1024.0f;
-                k1[1] = (_Float16)1024.0f;
-                a1 = __builtin_amdgcn_fdot2(xs[j][p], k1, a1, false);
-                a2 = __builtin_amdgcn_fdot2(xs[j][p], slot_pow2<BITS>(p), a2, false);
-            } else {
-                a1 = __builtin_amdgcn_fdot2(xs[j][p], slot_bias<BITS>(p, zdef), a1, false);
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int4_t v = src[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[j][4 * q + e] = as_half2((uint32_t)v[e]);
         }
-        c1[j] = a1;
-        c2[j] = a2;
+        const int rc = r < R ? r : R;               // c1[R] is written only by the dummy item: mask it
+        b1[j] = r < R ? c1[rc] : 0.f;
+        b2[j] = (PGZ && r < R) ? c2[rc] : 0.f;
     }
 
-    // 4. per column: dot products, per-run scale, wave reduction.
+    // 5. stream the wave's columns: compute column i while columns i+1..i+D-1 load
     float yout = 0.f;
+    for (int i0 = 0; i0 < ncw; i0 += D) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        float y = 0.f;
+        for (int q = 0; q < D; ++q) {
+            const int i = i0 + q;                     // columns past ncw compute on zeros
+            {
+                float y = 0.f;
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            uint32_t h[16];
-            run_to_half2<BITS>(d[c][j], h);
-            float a = 0.f;
+                for (int j = 0; j < RPL; ++j) {
+                    uint32_t h[16];
+                    run_to_half2<BITS>(d[q][j], h);
+                    float a = 0.f, a_odd = 0.f;
 #pragma unroll
-            for (int p = 0; p < 16; ++p) a = __builtin_amdgcn_fdot2(xs[j][p], as_half2(h[p]), a, false);
-            const float bias = PGZ ? fmaf((float)as_half(zv[c][j]), c2[j], c1[j]) : c1[j];
-            y = fmaf((float)as_half(sv[c][j]), a - bias, y);
+                    for (int p = 0; p < 16; p += 2) {
+                        a = __builtin_amdgcn_fdot2(xv[j][p], as_half2(h[p]), a, false);
+                        a_odd = __builtin_amdgcn_fdot2(xv[j][p + 1], as_half2(h[p + 1]), a_odd, false);
+                    }
+                    const float bias = PGZ ? fmaf((float)as_half(zv[q][j]), b2[j], b1[j]) : b1[j];
+                    y = fmaf((float)as_half(sv[q][j]), (a + a_odd) - bias, y);
+                }
+                issue(q, i + D);                      // refill this slot (zeros past the wave's columns)
+                y = wave_sum_dpp(y);
+                const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, y), 63));
+                if (lane == i) yout = tot;
+            }
         }
-        y = wave_sum(y);
-        if (lane == c) yout = y;
     }
-    if (lane < ncols) Y[n0 + lane] = f32_to_f16_bits(yout);
+    if (lane < ncw) Y[w + lane * W] = f32_to_f16_bits(yout);
 }
 
 // ---------------------------------------------------------------------------
@@ -181,7 +260,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
                                                         int M, int K, int N, int G, int passes)
 {
     __shared__ float red[8][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
     const uint32_t run_bytes = 4u * BITS;
@@ -297,8 +376,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
 // order + per-run bias sums); the tile's scales too.  Weight loads are issued
 // right after the X and scale loads, before any arithmetic.
 // ---------------------------------------------------------------------------
-template <int BITS, int T, int IPT, bool G128, bool PGZ>
-__global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restrict__ X,
+template <int BITS, int T, int IPT, int SPT, bool G128, bool PGZ>
+__global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restrict__ X,
                                                          const uint32_t *__restrict__ wq,
                                                          const uint16_t *__restrict__ s,
                                                          const uint16_t *__restrict__ z, uint16_t *__restrict__ Y,
@@ -307,7 +386,7 @@ __global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restr
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using P = RunPlan<BITS>;
     const int R = K >> 5, R4 = (R + 3) & ~3, TT = R4 >> 2, ng = K / G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = 64 * ks;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), nthreads = 64 * ks;
     const int g = lane >> 4, c = lane & 15;
     const int n0 = blockIdx.x * 16;
     const int nvalid = min(16, N - n0);
@@ -337,14 +416,20 @@ __global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restr
         const uint32_t off = (m < M && r < R) ? ((uint32_t)m * K + (uint32_t)r * 32u) * 2u : OOB;
         load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
     }
-    // 2. the tile's scales (and zero-points): 16 contiguous rows of ng halves
+    // 2. the tile's scales (and zero-points): 16 contiguous rows of ng halves, loaded
+    //    element by element (each 2-byte load is range-checked on its own, so the
+    //    ragged last tile reads zeros past its columns and nothing else)
     const uint32_t sbytes = (uint32_t)nvalid * ng * 2u;
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)n0 * ng, sbytes);
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z + (size_t)n0 * ng : s, PGZ ? sbytes : 0u);
-    uint32_t sraw[4], zraw[4];
-    const bool s_thread = tid < 2 * ng;   // 16 * ng halves = 2 * ng chunks of 16 B
-    load_dwords<LOAD_DEFAULT>(sr, s_thread ? (uint32_t)tid * 16u : OOB, sraw, 4);
-    if (PGZ) load_dwords<LOAD_DEFAULT>(zr, s_thread ? (uint32_t)tid * 16u : OOB, zraw, 4);
+    uint16_t sraw[SPT], zraw[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int si = tid + i * nthreads;
+        const uint32_t off = si < 16 * ng ? (uint32_t)si * 2u : OOB;
+        sraw[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        zraw[i] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : (uint16_t)0;
+    }
     __builtin_amdgcn_sched_barrier(0);
     // 3. this wave's packed weights, all in flight before any arithmetic
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)n0 * R * BITS, (uint32_t)nvalid * col_bytes);
@@ -389,58 +474,85 @@ __global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restr
             if (PGZ) c2[it] = a2;
         }
     }
-    {
-        const int si = s_thread ? 8 * tid : 16 * ng;   // 16 * ng = the dummy chunk
-        *reinterpret_cast<int4_t *>(sl + si) = int4_t{(int)sraw[0], (int)sraw[1], (int)sraw[2], (int)sraw[3]};
-        if (PGZ)
-            *reinterpret_cast<int4_t *>(zl + si) = int4_t{(int)zraw[0], (int)zraw[1], (int)zraw[2], (int)zraw[3]};
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int si0 = tid + i * nthreads;
+        const int si = si0 < 16 * ng ? si0 : 16 * ng;   // 16 * ng = the dummy slot
+        sl[si] = sraw[i];
+        if (PGZ) zl[si] = zraw[i];
     }
     if (tid < 4) reinterpret_cast<int4_t *>(smem + xs_bytes)[tid] = int4_t{0, 0, 0, 0};
     __syncthreads();
 
-    // 5. K steps: 4 MFMAs per step, bias as the accumulator's start value
+    // 5. K steps: 4 dependent MFMAs per step, the run bias as the accumulator's
+    //    start value.  Rule kept throughout: no load is issued while a chain is in
+    //    flight.  The LDS operands of step t+1 are read before chain t starts (so
+    //    they cannot land in registers chain t still reads), and chain t's result is
+    //    consumed before anything of step t+2 is loaded.
     const int r_row = c;                          // MFMA A row held by this lane
     const int am = r_row >> 2, ae = r_row & 3;    // (activation row, run) of that A row
     const bool a_live = (ae == g) && (am < M);
     const int om = g;                             // output rows 4g..4g+3 = (row g, runs 0..3)
     const int omc = min(om, M - 1);
-    float y = 0.f;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
+    const int nsteps = max(0, min(T, TT - tt0));
+
+    struct StepOps {
+        half8_t a[4];
+        float4_t init;
+        float sc[4];
+    };
+    auto load_step = [&](int t, StepOps &o) {
         const int tt = tt0 + t;
-        if (tt >= TT) break;                       // wave-uniform
-        uint32_t h[16];
-        run_to_half2<BITS>(d[t], h);
+        const uint32_t abase = a_live ? ((uint32_t)(am * R4 + 4 * tt + g) * 64u) : xs_bytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o.a[u] = *reinterpret_cast<const half8_t *>(smem + abase + 16u * u);
         const float4_t cb = *reinterpret_cast<const float4_t *>(c1 + omc * R4 + 4 * tt);
-        float4_t acc;
         if (PGZ) {
             const float4_t cz = *reinterpret_cast<const float4_t *>(c2 + omc * R4 + 4 * tt);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int gi = min(((4 * tt + e) * 32) / G, ng - 1);
-                acc[e] = -fmaf((float)as_half(zl[c * ng + gi]), cz[e], cb[e]);
+                o.init[e] = -fmaf((float)as_half(zl[c * ng + gi]), cz[e], cb[e]);
+                o.sc[e] = (float)as_half(sl[c * ng + gi]);
             }
         } else {
-            acc = -cb;
+            o.init = -cb;
+            if (G128) {
+                o.sc[0] = (float)as_half(sl[c * ng + (tt * 128) / G]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o.sc[e] = (float)as_half(sl[c * ng + min(((4 * tt + e) * 32) / G, ng - 1)]);
+            }
         }
-        const uint32_t abase = a_live ? ((uint32_t)(am * R4 + 4 * tt + g) * 64u) : xs_bytes;
+        if (PGZ && G128) o.sc[1] = o.sc[2] = o.sc[3] = o.sc[0];
+    };
+
+    float y = 0.f;
+    StepOps cur, nxt;
+    if (nsteps > 0) load_step(0, cur);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t >= nsteps) break;                    // wave-uniform
+        if (t + 1 < nsteps) load_step(t + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t h[16];
+        run_to_half2<BITS>(d[t], h);
+        float4_t acc = cur.init;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const half8_t a = *reinterpret_cast<const half8_t *>(smem + abase + 16u * u);
             const half8_t b = __builtin_bit_cast(half8_t, int4_t{(int)h[4 * u], (int)h[4 * u + 1],
                                                                  (int)h[4 * u + 2], (int)h[4 * u + 3]});
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.a[u], b, acc, 0, 0, 0);
         }
-        if (G128) {
-            const float sc = (float)as_half(sl[c * ng + (tt * 128) / G]);
-            y = fmaf(sc, (acc[0] + acc[1]) + (acc[2] + acc[3]), y);
+        __builtin_amdgcn_sched_barrier(0);
+        if (G128 && !PGZ) {
+            y = fmaf(cur.sc[0], (acc[0] + acc[1]) + (acc[2] + acc[3]), y);
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int gi = min(((4 * tt + e) * 32) / G, ng - 1);
-                y = fmaf((float)as_half(sl[c * ng + gi]), acc[e], y);
-            }
+            for (int e = 0; e < 4; ++e) y = fmaf(cur.sc[e], acc[e], y);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
     }
 
     // 6. fixed-order sum over the ks waves
@@ -457,24 +569,56 @@ __global__ __launch_bounds__(1024) void gemv_rows_kernel(const uint16_t *__restr
 // ---------------------------------------------------------------------------
 // Launch selection.
 // ---------------------------------------------------------------------------
-template <int BITS, bool PGZ>
-static hipError_t gemv_m1_launch(const GemvArgs &a, int rpl, hipStream_t st)
+static size_t m1_lds_bytes(int K, bool pgz)
 {
-    constexpr int CPW = 4;
-    const int waves = (a.N + CPW - 1) / CPW;
-    const dim3 block(256), grid((waves + 3) / 4);
-#define QMM_M1(RPL)                                                                                             \
-    hipLaunchKernelGGL((gemv_m1_kernel<BITS, RPL, CPW, PGZ>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.K, \
-                       a.N, a.G)
-    switch (rpl) {
-        case 1: QMM_M1(1); break;
-        case 2: QMM_M1(2); break;
-        case 4: QMM_M1(4); break;
-        case 8: QMM_M1(8); break;
-        default: return hipErrorInvalidValue;
+    const int R = K / 32;
+    return (size_t)R * 64 + 128 + 4u * (size_t)(R + 4) * (pgz ? 2 : 1);
+}
+
+// Workgroups for the M = 1 stream: one per CU (four waves, one per SIMD),
+// fewer when N is small, so every wave has at least one column.
+static int m1_grid(int N)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
     }
-#undef QMM_M1
+    return std::max(1, std::min(cus, (N + 3) / 4));
+}
+
+template <int BITS, int RPL, int D, int IPT, bool PGZ>
+static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
+{
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_m1_kernel<BITS, RPL, D, IPT, PGZ>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const size_t lds = m1_lds_bytes(a.K, PGZ);
+    const dim3 block(256), grid(m1_grid(a.N));
+    hipLaunchKernelGGL((gemv_m1_kernel<BITS, RPL, D, IPT, PGZ>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y, a.K,
+                       a.N, a.G);
     return hipGetLastError();
+}
+
+// M = 1 with K <= 16384 and at most 64 columns per wave: RPL = runs per lane
+// (1, 2, 4, 8), D = 8 / RPL columns in flight per wave.
+template <int BITS, bool PGZ>
+static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
+{
+    const int R = a.K / 32;
+    const int rpl_need = (R + 63) / 64;
+    if (rpl_need <= 1) return gemv_m1_go<BITS, 1, 8, 1, PGZ>(a, st);
+    if (rpl_need <= 2) return gemv_m1_go<BITS, 2, 4, 1, PGZ>(a, st);
+    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, 2, 1, PGZ>(a, st);
+    return gemv_m1_go<BITS, 8, 1, 2, PGZ>(a, st);
 }
 
 template <int BITS, bool PGZ>
@@ -511,20 +655,20 @@ static size_t rows_lds_bytes(int M, int K, int G, int ks, bool pgz)
     return b + (size_t)ks * 4 * 16 * 4;
 }
 
-template <int BITS, int T, int IPT, bool G128, bool PGZ>
+template <int BITS, int T, int IPT, int SPT, bool G128, bool PGZ>
 static hipError_t gemv_rows_go(const GemvArgs &a, int ks, size_t lds, hipStream_t st)
 {
     static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
     if (!attr_set) {
         hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, T, IPT, G128, PGZ>),
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, T, IPT, SPT, G128, PGZ>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const dim3 block(64 * ks), grid((a.N + 15) / 16);
-    hipLaunchKernelGGL((gemv_rows_kernel<BITS, T, IPT, G128, PGZ>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y,
-                       a.M, a.K, a.N, a.G, ks);
+    hipLaunchKernelGGL((gemv_rows_kernel<BITS, T, IPT, SPT, G128, PGZ>), grid, block, lds, st, a.X, a.wq, a.s, a.z,
+                       a.Y, a.M, a.K, a.N, a.G, ks);
     return hipGetLastError();
 }
 
@@ -532,10 +676,10 @@ template <int BITS, int IPT, bool G128, bool PGZ>
 static hipError_t gemv_rows_pick_t(const GemvArgs &a, int T, int ks, size_t lds, hipStream_t st)
 {
     switch (T) {
-        case 1: return gemv_rows_go<BITS, 1, IPT, G128, PGZ>(a, ks, lds, st);
-        case 2: return gemv_rows_go<BITS, 2, IPT, G128, PGZ>(a, ks, lds, st);
-        case 4: return gemv_rows_go<BITS, 4, IPT, G128, PGZ>(a, ks, lds, st);
-        default: return gemv_rows_go<BITS, 8, IPT, G128, PGZ>(a, ks, lds, st);
+        case 1: return gemv_rows_go<BITS, 1, IPT, 1, G128, PGZ>(a, ks, lds, st);
+        case 2: return gemv_rows_go<BITS, 2, IPT, 2, G128, PGZ>(a, ks, lds, st);
+        case 4: return gemv_rows_go<BITS, 4, IPT, 4, G128, PGZ>(a, ks, lds, st);
+        default: return gemv_rows_go<BITS, 8, IPT, 4, G128, PGZ>(a, ks, lds, st);
     }
 }
 
@@ -553,13 +697,20 @@ template <int BITS>
 static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
 {
     const int R = a.K / 32, TT = (R + 3) / 4;
+    if (a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
+        (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64)
+        return a.z ? gemv_m1_launch<BITS, true>(a, st) : gemv_m1_launch<BITS, false>(a, st);
     if (a.M <= 4) {
         int T = 1;
         while (T < 8 && T < TT) T <<= 1;
         const int ks = (TT + T - 1) / T;
         const size_t lds = rows_lds_bytes(a.M, a.K, a.G, ks, a.z != nullptr);
         const int R4 = (R + 3) & ~3;
-        if (ks <= 16 && lds <= 160 * 1024 && 2 * (a.K / a.G) <= 64 * ks) {
+        // scales per thread: 16 * ng halves over 64 * ks threads, within the SPT the
+        // instantiation for T carries (1, 2, 4, 4 for T = 1, 2, 4, 8; enough for any
+        // G at T <= 4 and for G >= 64 at T = 8)
+        const int spt_max = T == 1 ? 1 : T == 2 ? 2 : 4;
+        if (ks <= 8 && lds <= 160 * 1024 && 16 * (a.K / a.G) <= spt_max * 64 * ks) {
             if (a.M * R4 <= 64 * ks) return gemv_rows_pick<BITS, 1>(a, T, ks, lds, st);
             if (a.M * R4 <= 2 * 64 * ks) return gemv_rows_pick<BITS, 2>(a, T, ks, lds, st);
         }

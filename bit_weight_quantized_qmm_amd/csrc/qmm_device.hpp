@@ -44,9 +44,17 @@ __host__ __device__ constexpr float pow2neg(int p) { return 1.0f / float(1u << p
 // byte offset is past num_records read zeros and never fault), which is how
 // ragged column and K tails are handled without divergent branches.
 // ---------------------------------------------------------------------------
+// Every resource the kernels build is wave-uniform by construction; passing
+// base and size through readfirstlane says so to the compiler, which otherwise
+// may keep the descriptor in VGPRs and wrap each load in a readfirstlane loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    void *ub = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    const int ubytes = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, ubytes, 0x00020000);
 }
 
 // Cache policy bits for buffer loads: streamed weights are read once.
@@ -73,6 +81,11 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t o
         d[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, AUX);
     }
 }
+
+// Index of this wave inside its workgroup, as a wave-uniform (SGPR) value.
+// Plain threadIdx.x / 64 looks divergent to the compiler; a buffer resource
+// built from it would be wrapped in a readfirstlane loop around every load.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // fp32 sum over the 64 lanes of a wave; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float v)

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
                                                    int passes)
 {
     __shared__ float red[8][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int m0 = blockIdx.y * 16;
     const int R = K >> 5, ng = K / G, steps_per_group = G / 128;

@@ -100,15 +100,18 @@ def run_product(q, fn, c):
     return fn(dev(c["X"]), wq, dev(c["s"]), z, c["bits"], c["G"])
 
 
+GEMV_SHAPES = [(256, 40, 64), (96, 19, 32), (1024, 130, 128), (4096, 33, 32), (2048, 50, 256), (8192, 17, 128)]
+
+
 @pytest.mark.parametrize("bits", range(1, 9))
-@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 @pytest.mark.parametrize("pgz", [False, True])
-def test_gemv_small(q, orc, bits, M, pgz):
-    for (K, N, G) in ((256, 40, 64), (96, 19, 32), (1024, 130, 128)):
-        c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(91, bits, M + K + N), per_group_z=pgz)
-        Y = run_product(q, q.gemv, c)
-        ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
-        assert rel_err(Y, ref) <= TOL, (K, N, G)
+@pytest.mark.parametrize("K,N,G", GEMV_SHAPES, ids=lambda v: str(v))
+def test_gemv_small(q, orc, bits, M, pgz, K, N, G):
+    c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(91, bits, M + K + N), per_group_z=pgz)
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+    assert rel_err(Y, ref) <= TOL
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
