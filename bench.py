@@ -9,12 +9,13 @@ set larger than 1 GiB, so no launch finds its weights in the 256 MB Infinity
 Cache or the L2 (the pages' protocol clears the cache between runs; here every
 launch simply reads weights nothing else has touched recently).
 
-Timing: HIP events recorded on the launch stream around every launch (the
-stream is first held by a spin kernel so the whole timed region is queued
-before the GPU starts it).  `value` is packed-weight bytes per second over the
-timed region; the `roofline` object prices the dominant kernel's algorithmic
-bytes (packed weights + scales + x + y) per launch against its mean launch
-duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
+Timing: two HIP events on the launch stream (torch's current stream) bracket
+a region of back-to-back launches; the stream is first held by a spin kernel
+so the host queues the whole region before the GPU starts it.  `value` is
+packed-weight bytes per second over K steps.  Each kernel is then timed alone
+over K back-to-back launches; the `roofline` object prices the dominant
+kernel's algorithmic bytes (packed weights + scales + x + y) per launch
+against that mean launch duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
 prefill product (qmm_gemm) in TFLOP/s against the 2.5 PFLOP/s dense fp16 MFMA
 peak, and the CPU oracle timed on this host on a bounded sample.
 
@@ -62,33 +63,27 @@ def source_digest() -> str:
 
 
 class Timer:
-    """Per-launch HIP events on the current (launch) stream."""
+    """HIP events on the launch stream (torch's current stream) bracketing a
+    region of back-to-back launches.  The stream is first held by a spin
+    kernel so the host can queue the whole region before the GPU starts it;
+    the region then measures GPU time only (kernels plus the dispatch gaps
+    between consecutive kernels on one stream)."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.pairs = {}
 
-    def hold(self):
-        # keep the stream busy while the host queues the timed launches
-        self.torch.cuda._sleep(200_000_000)
-
-    def launch(self, key, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
+    def region_ms(self, launch, count):
+        torch = self.torch
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record()
-        fn()
+        for i in range(count):
+            launch(i)
         ev1.record()
-        self.pairs.setdefault(key, []).append((ev0, ev1))
-
-    def mean_ms(self, key):
-        p = self.pairs[key]
-        return sum(a.elapsed_time(b) for a, b in p) / len(p)
-
-    def span_ms(self, keys):
-        firsts = [self.pairs[k][0][0] for k in keys]
-        lasts = [self.pairs[k][-1][1] for k in keys]
-        first = firsts[0]
-        return max(first.elapsed_time(l) for l in lasts)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
 
 
 def decode_setup(torch, q, synthetic, bits):
@@ -186,28 +181,27 @@ def main():
         for d in decs:
             decode_launch(q, d)
     torch.cuda.synchronize()
+
+    # the step: three decode products (k = 3, 4, 6), back to back
     print(f"bench: timing {args.steps} decode steps", file=sys.stderr, flush=True)
-    timer.hold()
-    for _ in range(args.steps):
-        for d in decs:
-            timer.launch(("gemv", d["bits"]), lambda d=d: decode_launch(q, d))
-    torch.cuda.synchronize()
-    keys = [("gemv", d["bits"]) for d in decs]
-    span = timer.span_ms(keys)
+    span = timer.region_ms(lambda i: [decode_launch(q, d) for d in decs], args.steps)
     ms_per_step = span / args.steps
     wq_step = sum(d["wq_bytes"] for d in decs)
     value = wq_step / (ms_per_step * 1e-3) / 1e9
-    per_bits = {}
+
+    # each kernel on its own: mean launch duration over the same number of launches
+    per_bits, mean_ms = {}, {}
     for d in decs:
-        ms = timer.mean_ms(("gemv", d["bits"]))
+        ms = timer.region_ms(lambda i, d=d: decode_launch(q, d), args.steps) / args.steps
+        mean_ms[d["bits"]] = ms
         per_bits[str(d["bits"])] = {
             "us_per_launch": round(ms * 1e3, 3),
             "packed_GBs": round(d["wq_bytes"] / (ms * 1e-3) / 1e9, 1),
             "algorithmic_GBs": round(d["alg_bytes"] / (ms * 1e-3) / 1e9, 1),
             "packed_frac_of_peak": round(d["wq_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
-    dom = max(decs, key=lambda d: timer.mean_ms(("gemv", d["bits"])))
-    dom_ms = timer.mean_ms(("gemv", dom["bits"]))
+    dom = max(decs, key=lambda d: mean_ms[d["bits"]])
+    dom_ms = mean_ms[dom["bits"]]
     achieved = dom["alg_bytes"] / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(f"gemv_m1_k{dom['bits']}"),
@@ -226,13 +220,8 @@ def main():
     Y = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda:0")
     for _ in range(3):
         q.gemm(X, wq, s, None, 4, w["G"], out=Y)
-    torch.cuda.synchronize()
-    timer.hold()
     nrep = max(10, args.steps // 2)
-    for _ in range(nrep):
-        timer.launch("gemm", lambda: q.gemm(X, wq, s, None, 4, w["G"], out=Y))
-    torch.cuda.synchronize()
-    gms = timer.mean_ms("gemm")
+    gms = timer.region_ms(lambda i: q.gemm(X, wq, s, None, 4, w["G"], out=Y), nrep) / nrep
     flops = 2.0 * w["M"] * w["N"] * w["K"]
     tfs = flops / (gms * 1e-3) / 1e12
     gemm = {"workload": w["name"], "us_per_launch": round(gms * 1e3, 2), "TFLOPs": round(tfs, 1),
