@@ -52,11 +52,21 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# Sources each profiled kernel is built from: a counter run stays valid for a
+# kernel only while these files are unchanged.
+KERNEL_SOURCES = {
+    "gemv_m1": ("gemv.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
+    "gemm": ("gemm.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
+    "w4a8": ("w4a8.hip", "qmm_device.hpp", "launch.hpp"),
+}
+
+
+def source_digest(names=None) -> str:
+    """sha256 (16 hex digits) over the named kernel sources, all of them by default."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "bit_weight_quantized_qmm_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".inc")):
+        if name.endswith((".hip", ".hpp", ".cpp", ".inc")) and (names is None or name in names):
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
@@ -111,17 +121,21 @@ def decode_launch(q, d):
 
 
 def traffic_for(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
+    committed rocprofv3 counter runs, or None unless those runs were taken on
+    the kernel's current sources."""
     try:
         with open(PROFILE_TRAFFIC) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_digest") != source_digest():
-        return None
     e = t.get("kernels", {}).get(kernel_key)
-    return None if e is None else e.get("bytes_per_launch")
+    if e is None:
+        return None
+    family = e.get("family")
+    if family not in KERNEL_SOURCES or e.get("source_digest") != source_digest(KERNEL_SOURCES[family]):
+        return None
+    return e.get("bytes_per_launch")
 
 
 def cpu_baseline(synthetic, budget_s=12.0):
