@@ -137,15 +137,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     load_x(0, xraw);
     load_w(0, dcur, scur, zcur);
     store_x(0, xraw);
+    // Nothing stays in flight into the loop: the loop body then starts from the
+    // same wait state on every iteration (the waits the compiler inserts for a
+    // join of differently-pending paths would otherwise cover the prefetch).
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
     for (int tt = 0; tt < TT; ++tt) {
         const int cur = tt & 1;
-        const bool more = tt + 1 < TT;
-        if (more) {
-            load_x(tt + 1, xraw);
-            load_w(tt + 1, dnext, snext, znext);
-        }
+        // prefetch step tt + 1 (past the last step every load is out of range: zeros)
+        load_x(tt + 1, xraw);
+        load_w(tt + 1, dnext, snext, znext);
         // dequantise this step's 4 runs (one per N subtile) into B fragments
         half8_t bq[4][4];
 #pragma unroll
@@ -193,16 +195,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                     acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ns][u], acc[ms][ns], 0, 0, 0);
             }
         }
-        if (more) store_x(cur ^ 1, xraw);
+        store_x(cur ^ 1, xraw);
         __syncthreads();
-        if (more) {
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
+        for (int ns = 0; ns < 4; ++ns) {
 #pragma unroll
-                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
-                scur[ns] = snext[ns];
-                zcur[ns] = znext[ns];
-            }
+            for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
+            scur[ns] = snext[ns];
+            zcur[ns] = znext[ns];
         }
     }
 
