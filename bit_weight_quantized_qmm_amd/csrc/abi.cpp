@@ -37,7 +37,7 @@ qmm_status check_shape(const char *fn, int64_t M, int64_t K, int64_t N, int bits
         return fail(QMM_ERR_UNSUPPORTED, "%s: dimension beyond the supported range", fn);
     if ((K / 32) * N > (int64_t(1) << 31) - 256)
         return fail(QMM_ERR_UNSUPPORTED, "%s: problem beyond the supported range", fn);
-    if (((M + 255) / 256) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+    if (((M + 127) / 128) * ((N + 255) / 256) > (int64_t(1) << 31) - 1)   // GEMM tiles of 128 x 256
         return fail(QMM_ERR_UNSUPPORTED, "%s: problem beyond the supported range", fn);
     return QMM_OK;
 }

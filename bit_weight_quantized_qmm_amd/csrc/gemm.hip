@@ -8,11 +8,9 @@
 // run's half-slot order and scaled by 2^-p, so both MFMA operands are plain
 // 16-byte fragments.
 //
-// Workgroup tile 256 (M) x 128 (N), 4 waves as 2 x 2, wave tile 128 x 64 =
-// 8 x 4 MFMA tiles.  K advances 128 rows per step: lane group g (lanes
-// 16g..16g+15) of every MFMA owns run 4t+g.  Workgroups are mapped so that the
-// 8 XCDs each take a contiguous band of M tiles (their X rows stay in that
-// XCD's L2 while the packed weights stream).
+// Workgroup tile 128 (M) x 256 (N), 4 waves side by side in N, wave tile
+// 128 x 64 = 8 x 4 MFMA tiles.  K advances 128 rows per step: lane group g
+// (lanes 16g..16g+15) of every MFMA owns run 4t+g.
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -44,10 +42,30 @@ __device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs
     }
 }
 
-constexpr int GEMM_BM = 256, GEMM_BN = 128;
+constexpr int GEMM_BM = 128, GEMM_BN = 256;
 constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
+constexpr int GEMM_GROUP_M = 4;          // M tiles per band of the tile order
 constexpr uint32_t GEMM_OOB = 0x80000000u;
 
+// Tile order: workgroup ids go round-robin over the 8 XCDs, so XCD x gets a
+// contiguous range of the tile sequence; the sequence walks bands of
+// GEMM_GROUP_M M tiles column tile by column tile, so the workgroups resident
+// on one XCD share both X row tiles and weight column tiles in its L2.
+__device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &nt)
+{
+    const int total = mtiles * ntiles;
+    int pid = blockIdx.x;
+    if (total % 8 == 0) pid = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+    const int band = pid / (GEMM_GROUP_M * ntiles);
+    const int first = band * GEMM_GROUP_M;
+    const int rows = min(mtiles - first, GEMM_GROUP_M);
+    const int in_band = pid - band * GEMM_GROUP_M * ntiles;
+    mt = first + in_band % rows;
+    nt = in_band / rows;
+}
+
+// Workgroup tile 128 (M) x 256 (N): 4 waves side by side in N, each 128 x 64
+// = 8 x 4 MFMA tiles, so every weight run is dequantised by exactly one lane.
 template <int BITS, bool PGZ>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
@@ -57,35 +75,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     using P = RunPlan<BITS>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GEMM_BM * GEMM_ROWB];
 
-    // XCD-aware tile order: consecutive workgroup ids go round-robin over the 8
-    // XCDs, so give XCD x a contiguous range of tiles (M-major).
-    const int total = mtiles * ntiles;
-    int tile = blockIdx.x;
-    if (total % 8 == 0) tile = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
-    const int mt = tile / ntiles, nt = tile % ntiles;
+    int mt, nt;
+    gemm_tile(mtiles, ntiles, mt, nt);
     const int m0 = mt * GEMM_BM, n0 = nt * GEMM_BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
-    const int wm = wave & 1, wn = wave >> 1;
     const int R = K >> 5, ng = K / G, TT = (R + 3) >> 2;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const float zdef = (float)(1u << (BITS - 1));
 
-    // X: rows m0.. of the whole K range (OOB rows and runs read zeros).
+    // X: rows m0.. of the whole K range (rows past M and runs past K read zeros).
     const int mrows = min(GEMM_BM, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
     // Weights, scales, zero-points of this wave's 64 columns.
-    const int wn0 = n0 + wn * 64;
+    const int wn0 = n0 + wave * 64;
     const int wcols = max(0, min(64, N - wn0));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)min(wn0, N) * ng, (uint32_t)(wcols * ng * 2));
     const __amdgpu_buffer_rsrc_t zr =
         make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
 
-    auto load_x = [&](int tt, uint32_t (&raw)[4][16]) {
+    // X staging: 128 rows x 4 runs of 64 bytes per step, two (row, run) pieces per thread.
+    auto load_x = [&](int tt, uint32_t (&raw)[2][16]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int it = tid + 256 * i;
             const int row = it >> 2, gg = it & 3;
             const int run = 4 * tt + gg;
@@ -93,9 +107,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
         }
     };
-    auto store_x = [&](int buf, const uint32_t (&raw)[4][16]) {
+    auto store_x = [&](int buf, const uint32_t (&raw)[2][16]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int it = tid + 256 * i;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t xraw[4][16];
+    uint32_t xraw[2][16];
     uint32_t dcur[4][BITS], dnext[4][BITS];
     uint16_t scur[4], snext[4], zcur[4], znext[4];
     load_x(0, xraw);
@@ -143,6 +157,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
+    const uint8_t *abase0 = &lds[0][c * GEMM_ROWB + g * 64];
     for (int tt = 0; tt < TT; ++tt) {
         const int cur = tt & 1;
         // prefetch step tt + 1 (past the last step every load is out of range: zeros)
@@ -184,17 +199,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                 }
             }
         }
-        const uint8_t *abase = &lds[cur][(wm * 128 + c) * GEMM_ROWB + g * 64];
+        const uint8_t *abase = abase0 + cur * (GEMM_BM * GEMM_ROWB);
+        // All 32 A fragments of the step stay in registers while the MFMAs walk
+        // the four column tiles in turn, so dequantising tile ns + 1 overlaps the
+        // MFMAs of tile ns.
+        half8_t a[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
-                const half8_t a = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
+            for (int ms = 0; ms < 8; ++ms) a[u][ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ns][u], acc[ms][ns], 0, 0, 0);
-            }
-        }
+        for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int ms = 0; ms < 8; ++ms)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u][ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
+        // the X permutation waits for this step's prefetch: keep it after the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
         store_x(cur ^ 1, xraw);
         __syncthreads();
 #pragma unroll
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             const int col = wn0 + ns * 16 + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = m0 + wm * 128 + ms * 16 + 4 * g + i;
+                const int row = m0 + ms * 16 + 4 * g + i;
                 if (row < M && col < N) Y[(size_t)row * N + col] = f32_to_f16_bits(acc[ms][ns][i]);
             }
         }
