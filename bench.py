@@ -17,9 +17,11 @@ over K back-to-back launches; the `roofline` object prices the dominant
 kernel's algorithmic bytes (packed weights + scales + x + y) per launch
 against that mean launch duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
 prefill product (qmm_gemm) in TFLOP/s against the 2.5 PFLOP/s dense fp16 MFMA
-peak, and the CPU oracle timed on this host on a bounded sample.
+peak, the batched-decode (70B MLP-up shapes, M = 1, 8, 16, k = 1, 2, 5, 7, 8) and
+W4A8 (8B MLP shapes, M = 16) products as a "suite" object, and the CPU oracle
+timed on this host on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-suite]
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--suite", action="store_true", help="also print one line per parity workload")
+    ap.add_argument("--no-suite", action="store_true", help="skip the batched-decode and W4A8 timings")
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
@@ -164,6 +166,81 @@ def cpu_baseline(synthetic, budget_s=12.0):
                       f"fp64 dequant and fp64 dot products, {dt:.1f} s wall"}
 
 
+def rotating(torch, tensors):
+    """Enough copies of the weight-side tensors that the copies together exceed
+    1 GiB, so consecutive launches never find their weights in a cache."""
+    per = sum(t.numel() * t.element_size() for t in tensors)
+    copies = max(2, -(-ROTATE_BYTES // per))
+    return [tuple(t.clone() for t in tensors) for _ in range(copies)]
+
+
+def batched_suite(torch, q, synthetic, timer, reps):
+    """70B MLP-up batched decode (K 8192, N 28672, G 128, per-group z) at M = 1, 8, 16
+    for k = 1, 2, 5, 7, 8: us per launch and HBM GB/s of the algorithmic bytes."""
+    w = synthetic.BATCHED_70B
+    K, N, G = w["K"], w["N"], w["G"]
+    out = {}
+    for bits in w["bits"]:
+        c = synthetic.make_case(max(w["Ms"]), K, N, bits, G, synthetic.seed_for(3, bits), per_group_z=True,
+                                s_range=w["s_range"])
+        wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), bits)
+        bufs = rotating(torch, (wq, torch.from_numpy(c["s"]).to("cuda:0"), torch.from_numpy(c["z"]).to("cuda:0")))
+        del wq, c["codes"]
+        X = torch.from_numpy(c["X"]).to("cuda:0")
+        row = {}
+        for M in w["Ms"]:
+            x = X[:M].contiguous()
+            y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+            state = {"i": 0}
+
+            def launch(i, x=x, y=y, state=state):
+                b = bufs[state["i"] % len(bufs)]
+                state["i"] += 1
+                q.gemv(x, b[0], b[1], b[2], bits, G, out=y)
+
+            for i in range(3):
+                launch(i)
+            ms = timer.region_ms(launch, reps) / reps
+            wq_bytes = N * K * bits // 8
+            alg = wq_bytes + 2 * N * (K // G) * 2 + M * K * 2 + M * N * 2
+            row[f"M{M}"] = {"us": round(ms * 1e3, 2), "packed_GBs": round(wq_bytes / ms / 1e6, 1),
+                            "algorithmic_GBs": round(alg / ms / 1e6, 1),
+                            "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        out[f"k{bits}"] = row
+        del bufs
+        torch.cuda.empty_cache()
+    return {"workload": w["name"], "per_bits": out}
+
+
+def w4a8_suite(torch, q, synthetic, timer, reps):
+    """8B MLP W4A8 (M 16, K 4096, N 14336, G 128): int8 activations, 4-bit weights."""
+    w = synthetic.W4A8_8B
+    M, K, N, G = w["M"], w["K"], w["N"], w["G"]
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(5, 4), s_range=w["s_range"])
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
+    bufs = rotating(torch, (wq, torch.from_numpy(c["s"]).to("cuda:0")))
+    del wq
+    Xq = torch.from_numpy(c["Xq"]).to("cuda:0")
+    sx = torch.from_numpy(c["sx"]).to("cuda:0")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    state = {"i": 0}
+
+    def launch(i):
+        b = bufs[state["i"] % len(bufs)]
+        state["i"] += 1
+        q.gemm_w4a8(Xq, sx, b[0], b[1], None, G, out=y)
+
+    for i in range(3):
+        launch(i)
+    ms = timer.region_ms(launch, reps) / reps
+    wq_bytes = N * K // 2
+    alg = wq_bytes + N * (K // G) * 2 + M * K + M * 2 + M * N * 2
+    return {"workload": w["name"], "us": round(ms * 1e3, 2), "packed_GBs": round(wq_bytes / ms / 1e6, 1),
+            "algorithmic_GBs": round(alg / ms / 1e6, 1),
+            "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,6 +319,13 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": traffic_for("gemm_k4")}}
 
+    suite = None
+    if not args.no_suite:
+        print("bench: timing the batched-decode and W4A8 workloads", file=sys.stderr, flush=True)
+        reps = max(10, args.steps // 2)
+        suite = {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
+                 "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps)}
+
     cpu = None
     if not args.no_cpu:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -258,6 +342,7 @@ def main():
         "roofline": roofline,
         "per_bits": per_bits,
         "gemm_m2048": gemm,
+        "suite": suite,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
     }

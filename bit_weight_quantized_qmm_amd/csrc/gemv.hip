@@ -569,6 +569,231 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 // ---------------------------------------------------------------------------
 // Launch selection.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// M <= 16 on MFMA, G % 128 == 0, K <= 8192.  One v_mfma_f32_16x16x32_f16 tile
+// is 16 rows (X, zero past M) by 16 columns.  The B operand is the raw fp16
+// code pattern 1024 + q 2^p of each lane's run (no per-weight arithmetic past
+// the unpack); the A operand is X in slot order scaled by 2^-p.  Per 128-row
+// step (one group or part of one) the tile's products are
+//   acc = sum_k x'_k (1024 + q_k 2^p_k) - 1024 S1 - z S2,
+//   S1 = sum_k x'_k,  S2 = sum_k x_k,
+// the correction entering as one more MFMA whose A fragment carries S1 and S2
+// split into fp16 high and low parts and whose B fragment carries -1024 and
+// -z; then y += s * acc (BitLLM Sec. 2.2, eq. (5): w = (q - z) s, factored so
+// that the code-independent parts are applied once per step and group).
+//
+// A workgroup of 8 waves owns a range of consecutive 16-column tiles; wave w
+// owns K steps w*S .. w*S + S - 1 of every tile and keeps the A fragments of
+// that K slice in registers.  Units (tile, step) stream through a ring of D
+// weight loads in flight, each tile walked front to back along K; per batch
+// of T tiles the 8 partial tiles are added in LDS and written out.
+// ---------------------------------------------------------------------------
+static int num_cus();
+
+constexpr int MMA_WAVES = 8;   // waves per workgroup of the M <= 16 MFMA GEMV
+
+template <int BITS, int S, int T, int D, bool PGZ>
+__global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+                                                       const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
+                                                       uint16_t *__restrict__ Y, int M, int K, int N, int G, int tpw)
+{
+    __shared__ float red[MMA_WAVES][T][64][4];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int R = K >> 5, ng = K / G;
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
+    const int tiles = (N + 15) >> 4;
+    const int first = blockIdx.x * tpw;
+    const int last = min(tiles, first + tpw);
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)((size_t)N * col_bytes));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint32_t)(N * ng * 2));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
+    const float zdef = (float)(1u << (BITS - 1));
+
+    // X run of this lane for step t: row c, run 4 t + g (zeros past M or K)
+    auto load_xrun = [&](int t, uint32_t (&raw)[16]) {
+        const int run = 4 * t + g;
+        load_dwords<LOAD_DEFAULT>(xr, (run < R && c < M) ? ((uint32_t)c * K + (uint32_t)run * 32u) * 2u : OOB, raw, 16);
+    };
+    // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c,
+    // run 4 t + g of step t = wave * S + st.  Consecutive units walk one column
+    // tile through the wave's K slice, so every column is read front to back.
+    uint32_t d[D][BITS], sv[D], zv[D];
+    auto issue = [&](int unit, int tile0) {
+        const int slot = unit % D;
+        const int j = unit / S, st = unit % S;
+        const int t = wave * S + st;
+        const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
+        // a run past K reads other bits of the resource (or zeros past its
+        // end) and meets zero activations; the group index stays valid
+        const uint32_t grp = (uint32_t)min((t * 128) / G, ng - 1);
+        load_dwords<LOAD_STREAM>(wr, col * col_bytes + (uint32_t)(4 * t + g) * run_bytes, d[slot], BITS);
+        sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(sr, (col * (uint32_t)ng + grp) * 2u, 0, 0);
+        zv[slot] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, (col * (uint32_t)ng + grp) * 2u, 0, 0) : 0u;
+    };
+
+    // A fragments and correction fragments of the wave's K slice, once: they
+    // do not depend on the column tile.
+    half8_t A[S][4];
+    uint32_t AC[S][2];   // correction fragment of lane group 0: (S1 hi, S1 lo), (S2 hi, S2 lo)
+    {
+        uint32_t xa[S][16];
+#pragma unroll
+        for (int st = 0; st < S; ++st) load_xrun(wave * S + st, xa[st]);
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            half2_t xs[16];
+            x_slots<BITS>(xa[st], xs);
+            half2_t one2;
+            one2[0] = (_Float16)1.0f;
+            one2[1] = (_Float16)1.0f;
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                s1 = __builtin_amdgcn_fdot2(xs[p], one2, s1, false);
+                s2 = __builtin_amdgcn_fdot2(as_half2(xa[st][p]), one2, s2, false);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    A[st][u][2 * e] = xs[4 * u + e][0];
+                    A[st][u][2 * e + 1] = xs[4 * u + e][1];
+                }
+            // the step's four runs sit in lane groups 0..3 of the same row
+            s1 += __shfl_xor(s1, 16);
+            s1 += __shfl_xor(s1, 32);
+            s2 += __shfl_xor(s2, 16);
+            s2 += __shfl_xor(s2, 32);
+            const _Float16 s1h = (_Float16)s1, s2h = (_Float16)s2;
+            const _Float16 s1l = (_Float16)(s1 - (float)s1h), s2l = (_Float16)(s2 - (float)s2h);
+            half2_t p1, p2;
+            p1[0] = s1h;
+            p1[1] = s1l;
+            p2[0] = s2h;
+            p2[1] = s2l;
+            AC[st][0] = g == 0 ? as_u32(p1) : 0u;
+            AC[st][1] = g == 0 ? as_u32(p2) : 0u;
+        }
+    }
+
+    for (int tile0 = first; tile0 < last; tile0 += T) {
+#pragma unroll
+        for (int u = 0; u < D && u < S * T; ++u) issue(u, tile0);
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < S; ++st) {
+                const int unit = j * S + st, slot = unit % D;
+                uint32_t h[16];
+                run_to_half2<BITS>(d[slot], h);
+                half8_t bc;
+                {
+                    const _Float16 zero = (_Float16)0.0f;
+                    const _Float16 zz = PGZ ? as_half((uint16_t)zv[slot]) : (_Float16)zdef;
+                    bc[0] = g == 0 ? (_Float16)-1024.0f : zero;
+                    bc[1] = bc[0];
+                    bc[2] = g == 0 ? (_Float16)(-zz) : zero;
+                    bc[3] = bc[2];
+                    bc[4] = zero;
+                    bc[5] = zero;
+                    bc[6] = zero;
+                    bc[7] = zero;
+                }
+                const float sc = (float)as_half((uint16_t)sv[slot]);
+                half8_t b[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const half2_t hh = as_half2(h[4 * u + e]);
+                        b[u][2 * e] = hh[0];
+                        b[u][2 * e + 1] = hh[1];
+                    }
+                // The unpack's v_and_or_b32 is inline asm, which the compiler does
+                // not count as a VALU write when it spaces an MFMA that reads the
+                // result; fence the unpack off and give the MFMAs explicit wait
+                // states (k = 7 read stale B operands without them).
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_nop 7");
+                half8_t ac;
+                {
+                    const half2_t p1 = as_half2(AC[st][0]), p2 = as_half2(AC[st][1]);
+                    const _Float16 zero = (_Float16)0.0f;
+                    ac[0] = p1[0];
+                    ac[1] = p1[1];
+                    ac[2] = p2[0];
+                    ac[3] = p2[1];
+                    ac[4] = zero;
+                    ac[5] = zero;
+                    ac[6] = zero;
+                    ac[7] = zero;
+                }
+                float4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac, bc, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st][u], b[u], acc, 0, 0, 0);
+                if (unit + D < S * T) issue(unit + D, tile0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = fmaf(sc, acc[i], y[i]);
+            }
+            // lane (g, c) of a tile holds rows 4g..4g+3, column c
+            *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
+        }
+        // add the 8 waves' partial tiles
+        __syncthreads();
+        for (int o = threadIdx.x; o < T * 256; o += 64 * MMA_WAVES) {
+            const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
+            const int l = (m >> 2) * 16 + col, i = m & 3;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < MMA_WAVES; ++w) v += red[w][j][l][i];
+            const int n = 16 * (tile0 + j) + col;
+            if (m < M && n < N && tile0 + j < last) Y[(size_t)m * N + n] = f32_to_f16_bits(v);
+        }
+        __syncthreads();
+    }
+}
+
+template <int BITS, int S, int T, bool PGZ>
+static hipError_t gemv_mma_go(const GemvArgs &a, int grid, int tpw, hipStream_t st)
+{
+    // weight units in flight: about 32 dwords per lane, fewer when the K slice
+    // (S steps of A fragments) already holds most of the registers
+    constexpr int DMAX = S >= 8 ? 4 : 8;
+    constexpr int D0 = 32 / BITS < 4 ? 4 : (32 / BITS > DMAX ? DMAX : 32 / BITS);
+    constexpr int D = D0 < S * T ? D0 : S * T;
+    hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
+                       a.M, a.K, a.N, a.G, tpw);
+    return hipGetLastError();
+}
+
+template <int BITS, int S, bool PGZ>
+static hipError_t gemv_mma_pick_t(const GemvArgs &a, int grid, int tpw, hipStream_t st)
+{
+    if (tpw <= 1) return gemv_mma_go<BITS, S, 1, PGZ>(a, grid, tpw, st);
+    if (tpw <= 2) return gemv_mma_go<BITS, S, 2, PGZ>(a, grid, tpw, st);
+    if (tpw <= 4) return gemv_mma_go<BITS, S, 4, PGZ>(a, grid, tpw, st);
+    return gemv_mma_go<BITS, S, 8, PGZ>(a, grid, tpw, st);
+}
+
+// Requires G % 128 == 0 and K <= 8192 (8 waves x 8 steps of 128 rows).
+template <int BITS, bool PGZ>
+static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
+{
+    const int TT = (a.K / 32 + 3) / 4;                   // 128-row steps
+    const int steps = (TT + MMA_WAVES - 1) / MMA_WAVES;  // per wave
+    const int tiles = (a.N + 15) / 16;
+    const int tpw = std::max(1, (tiles + num_cus() - 1) / num_cus());
+    const int grid = (tiles + tpw - 1) / tpw;
+    if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ>(a, grid, tpw, st);
+    if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ>(a, grid, tpw, st);
+    if (steps <= 4) return gemv_mma_pick_t<BITS, 4, PGZ>(a, grid, tpw, st);
+    return gemv_mma_pick_t<BITS, 8, PGZ>(a, grid, tpw, st);
+}
+
 static size_t m1_lds_bytes(int K, bool pgz)
 {
     const int R = K / 32;
@@ -577,7 +802,7 @@ static size_t m1_lds_bytes(int K, bool pgz)
 
 // Workgroups for the M = 1 stream: one per CU (four waves, one per SIMD),
 // fewer when N is small, so every wave has at least one column.
-static int m1_grid(int N)
+static int num_cus()
 {
     static int cus = 0;
     if (cus == 0) {
@@ -588,8 +813,10 @@ static int m1_grid(int N)
         else
             cus = 256;
     }
-    return std::max(1, std::min(cus, (N + 3) / 4));
+    return cus;
 }
+
+static int m1_grid(int N) { return std::max(1, std::min(num_cus(), (N + 3) / 4)); }
 
 template <int BITS, int RPL, int D, int IPT, bool PGZ>
 static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
@@ -700,6 +927,8 @@ static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
     if (a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
         (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64)
         return a.z ? gemv_m1_launch<BITS, true>(a, st) : gemv_m1_launch<BITS, false>(a, st);
+    if (a.M >= 2 && a.G % 128 == 0 && a.K <= 64 * 128 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
+        return a.z ? gemv_mma_launch<BITS, true>(a, st) : gemv_mma_launch<BITS, false>(a, st);
     if (a.M <= 4) {
         int T = 1;
         while (T < 8 && T < TT) T <<= 1;

@@ -100,7 +100,8 @@ def run_product(q, fn, c):
     return fn(dev(c["X"]), wq, dev(c["s"]), z, c["bits"], c["G"])
 
 
-GEMV_SHAPES = [(256, 40, 64), (96, 19, 32), (1024, 130, 128), (4096, 33, 32), (2048, 50, 256), (8192, 17, 128)]
+GEMV_SHAPES = [(256, 40, 64), (96, 19, 32), (1024, 130, 128), (4096, 33, 32), (2048, 50, 256), (8192, 17, 128),
+               (384, 70, 128), (1152, 33, 128)]
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
@@ -133,20 +134,43 @@ def test_gemm_small(q, orc, bits, M):
         assert rel_err(Y, ref) <= TOL, (K, N, G, pgz)
 
 
-@pytest.mark.parametrize("fn", ["gemv", "gemm"])
-@pytest.mark.parametrize("bits", [1, 3, 4, 8])
-def test_codes_equal_zero_point_give_exact_zero(q, fn, bits):
-    K, N, G, M = 512, 70, 128, 5
+def _codes_at_zero_point(bits, M):
+    K, N, G = 512, 70, 128
     g = synthetic.rng(99 + bits)
     z = synthetic.zeros_uniform(g, bits, N, K // G)
     codes = np.repeat(z.astype(np.uint8).T, G, axis=0)
     c = dict(bits=bits, G=G, X=synthetic.fp16_normal(g, (M, K)), codes=codes,
              s=synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G)), z=z)
-    Y = run_product(q, getattr(q, fn), c)
-    assert not Y.float().abs().max().item()
     mid = dict(c, codes=np.full((K, N), 1 << (bits - 1), dtype=np.uint8), z=None)
-    Y = run_product(q, getattr(q, fn), mid)
-    assert not Y.float().abs().max().item()
+    return c, mid
+
+
+@pytest.mark.parametrize("bits", [1, 3, 4, 8])
+def test_codes_equal_zero_point_give_exact_zero(q, bits):
+    """q == z everywhere makes W == 0, so Y == 0.  The GEMM subtracts the
+    zero-point bias from every weight in fp16 before any rounding (an exact
+    difference), so it must return exact zeros."""
+    for c in _codes_at_zero_point(bits, 5):
+        Y = run_product(q, q.gemm, c)
+        assert not Y.float().abs().max().item()
+
+
+@pytest.mark.parametrize("bits", [1, 3, 4, 8])
+@pytest.mark.parametrize("M", [1, 5])
+def test_codes_equal_zero_point_gemv_bounded(q, bits, M):
+    """Same invariant on the GEMV paths, which remove the bias from a sum: the
+    raw products x' (1024 + q 2^p) are summed in fp32 and the matching
+    sum x' (1024 + z 2^p) (per run at M = 1; as 1024 S1 + z S2 per 128-row step
+    at M >= 2) is subtracted, so q == z leaves only rounding residue.  Bound per
+    output: 2^-16 s (1024 + z) sum|x| over each group (fp32 sums of up to 160
+    products, and an fp16 high/low split of S1 and S2, both far inside 2^-16)."""
+    for c in _codes_at_zero_point(bits, M):
+        Y = run_product(q, q.gemv, c).float().cpu().numpy()
+        G = c["G"]
+        z = c["z"] if c["z"] is not None else np.full(c["s"].shape, 2.0 ** (bits - 1))
+        ax = np.abs(c["X"].astype(np.float64)).reshape(c["X"].shape[0], -1, G).sum(2)   # [M, ng]
+        bound = 2.0 ** -16 * ax @ (c["s"].astype(np.float64) * (1024.0 + z.astype(np.float64))).T
+        assert np.all(np.abs(Y) <= bound), float((np.abs(Y) / bound).max())
 
 
 def test_deterministic(q):
