@@ -14,6 +14,8 @@
 // Workgroup: 8 waves split K for one 16-column x 16-row tile; a K step is 128
 // rows = 4 runs, lane group g owning run 4t+g.  Requires G % 128 == 0 so that
 // every K step lies inside one group.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -137,6 +139,184 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming form for K <= 8192 and G in {128, 256, 512, 1024} (G / 128 steps
+// per group, never more than a wave's K slice): 8 waves per workgroup, wave w
+// owns K steps w*S .. w*S + S - 1 (128 rows each) and keeps their int8 A
+// fragments and the row sums of Xq (from the MFMA against ones) in registers.
+// Units (tile, step) stream through a ring of D weight loads, each column tile
+// walked front to back along K; a group's int32 sum A = raw - z * sum(Xq) is
+// exact, optionally dumped, and scaled into the fp32 partial y; per batch of T
+// tiles the 8 partial tiles are added in LDS.
+// ---------------------------------------------------------------------------
+template <int S, int T, int D, bool PGZ>
+__global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
+                                                          const uint32_t *__restrict__ wq,
+                                                          const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
+                                                          uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out,
+                                                          int M, int K, int N, int G, int tpw)
+{
+    __shared__ float red[8][T][64][4];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int m0 = blockIdx.y * 16;
+    const int mrows = min(16, M - m0);
+    const int R = K >> 5, ng = K / G, TT = R >> 2, sp = G >> 7;
+    const uint32_t col_bytes = (uint32_t)R * 16u;
+    const int tiles = (N + 15) >> 4;
+    const int first = blockIdx.x * tpw;
+    const int last = min(tiles, first + tpw);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)((size_t)N * col_bytes));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint32_t)(N * ng * 2));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
+    const int4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+    uint32_t d[D][4], sv[D], zv[D];
+    auto issue = [&](int unit, int tile0) {
+        const int slot = unit % D;
+        const int j = unit / S, st = unit % S;
+        const int t = wave * S + st;
+        const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
+        // a step past K reads other bits of the resource (or zeros past its end)
+        // and meets zero activations; the group index stays valid
+        const uint32_t grp = (uint32_t)min(t / sp, ng - 1);
+        load_dwords<LOAD_STREAM>(wr, col * col_bytes + (uint32_t)(4 * t + g) * 16u, d[slot], 4);
+        sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(sr, (col * (uint32_t)ng + grp) * 2u, 0, 0);
+        zv[slot] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, (col * (uint32_t)ng + grp) * 2u, 0, 0) : 0u;
+    };
+
+    // A fragments of step st: lane (g, c) holds row c, run 4 t + g (32 bytes), bytes
+    // permuted to the nibble order of the B operand (even codes, then odd codes)
+    int4_t a[S][2], sxg[S];
+    {
+        uint32_t x[S][8];
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int run = 4 * (wave * S + st) + g;
+            load_dwords<LOAD_DEFAULT>(xr, (run < R && c < mrows) ? (uint32_t)c * K + (uint32_t)run * 32u : W_OOB, x[st], 8);
+        }
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                int4_t av;
+                av[0] = (int)__builtin_amdgcn_perm(x[st][4 * v + 1], x[st][4 * v], 0x06040200u);
+                av[1] = (int)__builtin_amdgcn_perm(x[st][4 * v + 1], x[st][4 * v], 0x07050301u);
+                av[2] = (int)__builtin_amdgcn_perm(x[st][4 * v + 3], x[st][4 * v + 2], 0x06040200u);
+                av[3] = (int)__builtin_amdgcn_perm(x[st][4 * v + 3], x[st][4 * v + 2], 0x07050301u);
+                a[st][v] = av;
+            }
+            const int4_t zero4 = {0, 0, 0, 0};
+            sxg[st] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][1], ones,
+                                                             __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][0], ones, zero4, 0, 0, 0),
+                                                             0, 0, 0);
+        }
+    }
+
+    for (int tile0 = first; tile0 < last; tile0 += T) {
+#pragma unroll
+        for (int u = 0; u < D && u < S * T; ++u) issue(u, tile0);
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
+            int4_t graw = {0, 0, 0, 0}, gsx = {0, 0, 0, 0};
+            const int n = 16 * (tile0 + j) + c;
+#pragma unroll
+            for (int st = 0; st < S; ++st) {
+                const int unit = j * S + st, slot = unit % D;
+                const int t = wave * S + st;
+                int4_t raw = {0, 0, 0, 0};
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const uint32_t da = d[slot][2 * v], db = d[slot][2 * v + 1];
+                    int4_t bv;
+                    bv[0] = (int)(da & 0x0f0f0f0fu);
+                    bv[1] = (int)((da >> 4) & 0x0f0f0f0fu);
+                    bv[2] = (int)(db & 0x0f0f0f0fu);
+                    bv[3] = (int)((db >> 4) & 0x0f0f0f0fu);
+                    raw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][v], bv, raw, 0, 0, 0);
+                }
+                graw += raw;
+                gsx += sxg[st];
+                const int zz = PGZ ? (int)(float)as_half((uint16_t)zv[slot]) : 8;
+                const float sc = (float)as_half((uint16_t)sv[slot]);
+                if (unit + D < S * T) issue(unit + D, tile0);
+                if ((t + 1) % sp == 0 && t < TT) {   // the group ends with this step
+                    const int grp = t / sp;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int A = graw[i] - zz * gsx[i];
+                        const int row = 4 * g + i;
+                        if (acc_out && row < mrows && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A;
+                        y[i] = fmaf(sc, (float)A, y[i]);
+                    }
+                    graw = int4_t{0, 0, 0, 0};
+                    gsx = int4_t{0, 0, 0, 0};
+                }
+            }
+            // lane (g, c) of a tile holds rows 4g..4g+3, column c
+            *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
+        }
+        __syncthreads();
+        for (int o = threadIdx.x; o < T * 256; o += 512) {
+            const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
+            const int l = (m >> 2) * 16 + col, i = m & 3;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) v += red[w][j][l][i];
+            const int n = 16 * (tile0 + j) + col;
+            if (m < mrows && n < N && tile0 + j < last) {
+                const float sxm = (float)as_half(sx[m0 + m]);
+                Y[(size_t)(m0 + m) * N + n] = f32_to_f16_bits(sxm * v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int S, int T, bool PGZ>
+static hipError_t w4a8_stream_go(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
+{
+    constexpr int D = S * T < 8 ? S * T : 8;
+    hipLaunchKernelGGL((w4a8_stream_kernel<S, T, D, PGZ>), grid, dim3(512), 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc,
+                       a.M, a.K, a.N, a.G, tpw);
+    return hipGetLastError();
+}
+
+template <int S, bool PGZ>
+static hipError_t w4a8_stream_pick_t(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
+{
+    if (tpw <= 1) return w4a8_stream_go<S, 1, PGZ>(a, grid, tpw, st);
+    if (tpw <= 2) return w4a8_stream_go<S, 2, PGZ>(a, grid, tpw, st);
+    if (tpw <= 4) return w4a8_stream_go<S, 4, PGZ>(a, grid, tpw, st);
+    return w4a8_stream_go<S, 8, PGZ>(a, grid, tpw, st);
+}
+
+// Returns hipErrorNotSupported when the shape needs more than 8 steps per wave.
+template <bool PGZ>
+static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
+{
+    const int TT = a.K / 128, sp = a.G / 128;
+    int S = 1;
+    while (S < 8 && (S * 8 < TT || S < sp)) S <<= 1;
+    if (S * 8 < TT || S < sp) return hipErrorNotSupported;
+    const int mtiles = (a.M + 15) / 16;
+    if (mtiles > 65535) return hipErrorNotSupported;
+    const int tiles = (a.N + 15) / 16;
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_m = std::max(1, cus / mtiles);
+    const int tpw = std::max(1, (tiles + per_m - 1) / per_m);
+    const dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)mtiles);
+    switch (S) {
+        case 1: return w4a8_stream_pick_t<1, PGZ>(a, grid, tpw, st);
+        case 2: return w4a8_stream_pick_t<2, PGZ>(a, grid, tpw, st);
+        case 4: return w4a8_stream_pick_t<4, PGZ>(a, grid, tpw, st);
+        default: return w4a8_stream_pick_t<8, PGZ>(a, grid, tpw, st);
+    }
+}
+
 template <bool PGZ>
 static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipStream_t st)
 {
@@ -159,6 +339,10 @@ static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipSt
 hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st)
 {
     if (a.G % 128 != 0 || a.G > 1024) return hipErrorNotSupported;
+    if (a.K <= 8192 && (size_t)a.N * (a.K / 32) * 16 < 0x7fffffffu) {
+        const hipError_t e = a.z ? w4a8_stream_launch<true>(a, st) : w4a8_stream_launch<false>(a, st);
+        if (e != hipErrorNotSupported) return e;
+    }
     const int R = a.K / 32;
     const int TT = (R + 3) / 4;
     int T = 1;

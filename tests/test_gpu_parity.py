@@ -282,6 +282,19 @@ def test_w4a8_small(q, orc, M, G, pgz):
     assert rel_err(Y, ref) <= TOL
 
 
+@pytest.mark.parametrize("M,K,N,G,pgz", [(3, 2048, 50, 512, True), (16, 2048, 33, 1024, False),
+                                          (8, 8192, 40, 128, True), (2, 16384, 20, 256, False),
+                                          (40, 3072, 65, 128, True)])
+def test_w4a8_shapes(q, orc, M, K, N, G, pgz):
+    """Groups spanning several 128-row steps, K slices that leave waves idle, and
+    K beyond the streaming kernel's register slice (the tiled kernel)."""
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(96, M, K // 128), per_group_z=pgz)
+    Y, acc = run_w4a8(q, c)
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], c["z"], G)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
+
+
 def test_w4a8_extreme_activations(q, orc):
     """-128 everywhere and codes at the ends of their range: int32 sums still exact."""
     M, K, N, G = 16, 512, 40, 128
