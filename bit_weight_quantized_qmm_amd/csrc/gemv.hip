@@ -69,12 +69,12 @@ constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every resource w
 // ---------------------------------------------------------------------------
 // M = 1: split-K across the 64 lanes of a wave, one 32-code run per lane and
 // load, so a wave's load of one column is one contiguous k*256-byte stretch
-// (the access pattern of a plain streaming read).  A workgroup of 4 waves owns
-// 4*CPW consecutive columns.  Once per workgroup, X is staged in LDS in the
-// unpack's slot order (scaled by 2^-p) with per-run bias sums, and the
-// columns' scales too; the activation and scale loads go out before the
-// weight loads, so the staging overlaps the weight stream.  Lane l owns runs
-// l, l+64, ... (RPL of them); per run 16 v_dot2_f32_f16 give
+// (the access pattern of a plain streaming read).  Persistent: one workgroup
+// of 4 waves per CU, wave w of W takes columns w, w + W, ... and keeps D
+// columns of loads in flight.  Once per workgroup X is staged in LDS in the
+// unpack's slot order (scaled by 2^-p) with the per-run bias sums; the X loads
+// go out before the weight loads, so the staging overlaps the weight stream.
+// Lane l owns runs l, l+64, ... (RPL of them); per run 16 v_dot2_f32_f16 give
 // a = sum x'(1024 + q 2^p), and y += s_g * (a - bias).  A DPP reduction
 // finishes each column.
 // ---------------------------------------------------------------------------

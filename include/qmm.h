@@ -85,17 +85,27 @@ qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, 
                       qmm_stream stream);
 
 /* Decode-shaped product, 1 <= M <= 16 (else QMM_ERR_INVALID_ARG):
- * Y = X . dequant(Wq), fp32 accumulation.  M == 1 runs a split-K VALU kernel
- * (v_dot2 on fp16 code pairs, per-group scale applied to each 32-code partial
- * sum); 2 <= M <= 16 runs f16 MFMA with M padded to 16.  Eq. (5) of BitLLM
- * Sec. 2.2 with per-group s, z. */
+ * Y = X . dequant(Wq), fp32 accumulation.  Eq. (5) of BitLLM Sec. 2.2 with
+ * per-group s, z, factored so that the zero-point bias leaves a sum:
+ *   M == 1: a split-K VALU kernel (v_dot2 of the activations, scaled by 2^-p,
+ *           with the fp16 code patterns 1024 + q 2^p; the bias of each 32-code
+ *           run is subtracted from its partial sum, which is then scaled).
+ *   2 <= M <= 16 with G % 128 == 0 and K <= 8192: f16 MFMA with M padded to
+ *           16, the raw code patterns as B operand and one correction MFMA per
+ *           128 rows of K.
+ *   other shapes: f16 MFMA on weights dequantised in registers.
+ * Because the bias is removed from fp32 sums, codes equal to their zero-point
+ * give outputs within rounding of 0 (about 2^-16 of s (1024 + z) sum|x| per
+ * group), not exact zeros; qmm_gemm subtracts it per weight and returns exact
+ * zeros there. */
 qmm_status qmm_gemv(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
                     qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
                     qmm_stream stream);
 
 /* Same arguments and result as qmm_gemv for any M >= 1: f16 MFMA (fp32
- * accumulation) on weights dequantised in registers, X staged through LDS.
- * Intended for large M (prefill). */
+ * accumulation) on weights dequantised in registers ((q - z) 2^p formed by an
+ * exact fp16 subtraction, then one rounding multiply by s), X staged through
+ * LDS in 128 x 256 output tiles.  Intended for large M (prefill). */
 qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
                     qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
                     qmm_stream stream);
@@ -107,7 +117,8 @@ qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
  * computed with i8 MFMA.  Xq is symmetric int8 (no activation zero-point; -128
  * is accepted).  z must be integer-valued in [0, 15] (NULL = 8).  acc_out is
  * NULL or an int32 [M][K/G][N] array that receives A (for verification).
- * 1 <= M; QMM_ERR_UNSUPPORTED if M > 16 * 65535. */
+ * 1 <= M; G must be 128, 256, 512 or 1024 (QMM_ERR_UNSUPPORTED otherwise, and
+ * if M > 16 * 65535 or the dump would exceed 2^31 - 1 elements). */
 qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
                          const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K,
                          int64_t N, int64_t G, qmm_stream stream);
