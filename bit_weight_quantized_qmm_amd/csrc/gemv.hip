@@ -582,56 +582,81 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 // -z; then y += s * acc (BitLLM Sec. 2.2, eq. (5): w = (q - z) s, factored so
 // that the code-independent parts are applied once per step and group).
 //
-// A workgroup of 8 waves owns a range of consecutive 16-column tiles; wave w
+// A workgroup of 8 waves owns tpw <= T consecutive 16-column tiles; wave w
 // owns K steps w*S .. w*S + S - 1 of every tile and keeps the A fragments of
-// that K slice in registers.  Units (tile, step) stream through a ring of D
-// weight loads in flight, each tile walked front to back along K; per batch
-// of T tiles the 8 partial tiles are added in LDS and written out.
+// that K slice in registers.  The s and z of the workgroup's columns are
+// staged once in LDS (read along the group index, so every load is a whole
+// column's run of groups), which leaves only the weight runs in the per-unit
+// stream: units (tile, step) pass through a ring of D weight loads in flight,
+// each tile walked front to back along K.  At the end the 8 waves' partial
+// tiles are added in LDS and written out.
 // ---------------------------------------------------------------------------
 static int num_cus();
 
 constexpr int MMA_WAVES = 8;   // waves per workgroup of the M <= 16 MFMA GEMV
+constexpr int MMA_MAXNG = 64;  // groups per column: K <= 8192, G >= 128
 
 template <int BITS, int S, int T, int D, bool PGZ>
 __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                        const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                        uint16_t *__restrict__ Y, int M, int K, int N, int G, int tpw)
 {
+    static_assert(S % D == 0 || D % S == 0, "ring slots must stay compile-time indexes");
     __shared__ float red[MMA_WAVES][T][64][4];
+    // s | z << 16 of (group, column) for the workgroup's columns, group-major;
+    // the odd row stride keeps the transposing writes free of bank conflicts
+    constexpr int SZW = T * 16 + 1;
+    __shared__ uint32_t sz[MMA_MAXNG * SZW];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int tiles = (N + 15) >> 4;
-    const int first = blockIdx.x * tpw;
-    const int last = min(tiles, first + tpw);
+    const int tile0 = blockIdx.x * tpw;
+    const int ntile = min(tpw, tiles - tile0);   // 1 <= ntile <= T
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)((size_t)N * col_bytes));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint32_t)(N * ng * 2));
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
-    const float zdef = (float)(1u << (BITS - 1));
+    const uint32_t zdef_bits = (uint32_t)as_u16((_Float16)(float)(1u << (BITS - 1)));
+
+    // s and z of the workgroup's columns: wave w reads columns w, w + 8, ...,
+    // lane l holding group l (past ng, or past the workgroup's columns: zeros)
+    constexpr int SZE = T * 16 / MMA_WAVES;
+    uint32_t sraw[SZE], zraw[SZE];
+#pragma unroll
+    for (int e = 0; e < SZE; ++e) {
+        const int cl = wave + MMA_WAVES * e;
+        const uint32_t off = (lane < ng && cl < 16 * ntile) ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)lane) * 2u : OOB;
+        sraw[e] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        zraw[e] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : zdef_bits;
+    }
+
+    // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c,
+    // run 4 t + g of step t = wave * S + st.  Consecutive units walk one column
+    // tile through the wave's K slice, so every column is read front to back.
+    // A run past K reads other bits of the resource (or zeros past its end)
+    // and meets zero activations; units past the workgroup's tiles load nothing.
+    uint32_t d[D][BITS];
+    auto issue = [&](int j, int st, int slot) {
+        const int t = wave * S + st;
+        const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
+        load_dwords<LOAD_STREAM>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * run_bytes : OOB, d[slot], BITS);
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) issue(u / S, u % S, u);
+
+#pragma unroll
+    for (int e = 0; e < SZE; ++e) {
+        const int cl = wave + MMA_WAVES * e;
+        if (lane < ng) sz[lane * SZW + cl] = (sraw[e] & 0xffffu) | (zraw[e] << 16);
+    }
 
     // X run of this lane for step t: row c, run 4 t + g (zeros past M or K)
     auto load_xrun = [&](int t, uint32_t (&raw)[16]) {
         const int run = 4 * t + g;
         load_dwords<LOAD_DEFAULT>(xr, (run < R && c < M) ? ((uint32_t)c * K + (uint32_t)run * 32u) * 2u : OOB, raw, 16);
-    };
-    // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c,
-    // run 4 t + g of step t = wave * S + st.  Consecutive units walk one column
-    // tile through the wave's K slice, so every column is read front to back.
-    uint32_t d[D][BITS], sv[D], zv[D];
-    auto issue = [&](int unit, int tile0) {
-        const int slot = unit % D;
-        const int j = unit / S, st = unit % S;
-        const int t = wave * S + st;
-        const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
-        // a run past K reads other bits of the resource (or zeros past its
-        // end) and meets zero activations; the group index stays valid
-        const uint32_t grp = (uint32_t)min((t * 128) / G, ng - 1);
-        load_dwords<LOAD_STREAM>(wr, col * col_bytes + (uint32_t)(4 * t + g) * run_bytes, d[slot], BITS);
-        sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(sr, (col * (uint32_t)ng + grp) * 2u, 0, 0);
-        zv[slot] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, (col * (uint32_t)ng + grp) * 2u, 0, 0) : 0u;
     };
 
     // A fragments and correction fragments of the wave's K slice, once: they
@@ -678,22 +703,27 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
             AC[st][1] = g == 0 ? as_u32(p2) : 0u;
         }
     }
+    __syncthreads();
 
-    for (int tile0 = first; tile0 < last; tile0 += T) {
+    // UT tiles per loop iteration keep every ring slot a compile-time index
+    constexpr int UT = D > S ? D / S : 1;
+#pragma unroll 1
+    for (int jb = 0; jb < ntile; jb += UT) {
 #pragma unroll
-        for (int u = 0; u < D && u < S * T; ++u) issue(u, tile0);
-#pragma unroll
-        for (int j = 0; j < T; ++j) {
+        for (int jj = 0; jj < UT; ++jj) {
+            const int j = jb + jj;
             float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < S; ++st) {
-                const int unit = j * S + st, slot = unit % D;
+                const int slot = (jj * S + st) % D;
+                const int t = wave * S + st;
+                const uint32_t szv = sz[min((t * 128) / G, ng - 1) * SZW + 16 * j + c];
                 uint32_t h[16];
                 run_to_half2<BITS>(d[slot], h);
                 half8_t bc;
                 {
                     const _Float16 zero = (_Float16)0.0f;
-                    const _Float16 zz = PGZ ? as_half((uint16_t)zv[slot]) : (_Float16)zdef;
+                    const _Float16 zz = as_half((uint16_t)(szv >> 16));
                     bc[0] = g == 0 ? (_Float16)-1024.0f : zero;
                     bc[1] = bc[0];
                     bc[2] = g == 0 ? (_Float16)(-zz) : zero;
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                     bc[6] = zero;
                     bc[7] = zero;
                 }
-                const float sc = (float)as_half((uint16_t)sv[slot]);
+                const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
                 half8_t b[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
@@ -735,35 +765,38 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                 float4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac, bc, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st][u], b[u], acc, 0, 0, 0);
-                if (unit + D < S * T) issue(unit + D, tile0);
+                // refill the slot with the unit D ahead (past the tiles: no load)
+                issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = fmaf(sc, acc[i], y[i]);
             }
             // lane (g, c) of a tile holds rows 4g..4g+3, column c
             *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
         }
-        // add the 8 waves' partial tiles
-        __syncthreads();
-        for (int o = threadIdx.x; o < T * 256; o += 64 * MMA_WAVES) {
-            const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
-            const int l = (m >> 2) * 16 + col, i = m & 3;
-            float v = 0.f;
+    }
+    // add the 8 waves' partial tiles
+    __syncthreads();
+    for (int o = threadIdx.x; o < ntile * 256; o += 64 * MMA_WAVES) {
+        const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
+        const int l = (m >> 2) * 16 + col, i = m & 3;
+        float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < MMA_WAVES; ++w) v += red[w][j][l][i];
-            const int n = 16 * (tile0 + j) + col;
-            if (m < M && n < N && tile0 + j < last) Y[(size_t)m * N + n] = f32_to_f16_bits(v);
-        }
-        __syncthreads();
+        for (int w = 0; w < MMA_WAVES; ++w) v += red[w][j][l][i];
+        const int n = 16 * (tile0 + j) + col;
+        if (m < M && n < N) Y[(size_t)m * N + n] = f32_to_f16_bits(v);
     }
 }
+
+// Weight units in flight per wave: a power of two that divides, or is a
+// multiple of, the steps per tile.  The depth changes little once s and z come
+// from LDS; these are the fastest measured on the 70B MLP-up shape (K 8192,
+// N 28672) at M = 8 and 16 (wider codes leave fewer free registers).
+__host__ __device__ constexpr int mma_ring(int bits) { return bits <= 3 || bits == 7 ? 8 : bits == 8 ? 2 : 4; }
 
 template <int BITS, int S, int T, bool PGZ>
 static hipError_t gemv_mma_go(const GemvArgs &a, int grid, int tpw, hipStream_t st)
 {
-    // weight units in flight: about 32 dwords per lane, fewer when the K slice
-    // (S steps of A fragments) already holds most of the registers
-    constexpr int DMAX = S >= 8 ? 4 : 8;
-    constexpr int D0 = 32 / BITS < 4 ? 4 : (32 / BITS > DMAX ? DMAX : 32 / BITS);
+    constexpr int D0 = mma_ring(BITS);
     constexpr int D = D0 < S * T ? D0 : S * T;
     hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
                        a.M, a.K, a.N, a.G, tpw);
@@ -779,14 +812,16 @@ static hipError_t gemv_mma_pick_t(const GemvArgs &a, int grid, int tpw, hipStrea
     return gemv_mma_go<BITS, S, 8, PGZ>(a, grid, tpw, st);
 }
 
-// Requires G % 128 == 0 and K <= 8192 (8 waves x 8 steps of 128 rows).
+// Requires G % 128 == 0 and K <= 8192 (8 waves x 8 steps of 128 rows).  One
+// batch of at most 8 tiles per workgroup; past 8 x (CU count) tiles the
+// workgroups run in several rounds.
 template <int BITS, bool PGZ>
 static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
 {
     const int TT = (a.K / 32 + 3) / 4;                   // 128-row steps
     const int steps = (TT + MMA_WAVES - 1) / MMA_WAVES;  // per wave
     const int tiles = (a.N + 15) / 16;
-    const int tpw = std::max(1, (tiles + num_cus() - 1) / num_cus());
+    const int tpw = std::min(8, std::max(1, (tiles + num_cus() - 1) / num_cus()));
     const int grid = (tiles + tpw - 1) / tpw;
     if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ>(a, grid, tpw, st);
     if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ>(a, grid, tpw, st);
