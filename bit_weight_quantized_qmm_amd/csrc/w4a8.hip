@@ -144,10 +144,11 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
 // per group, never more than a wave's K slice): 8 waves per workgroup, wave w
 // owns K steps w*S .. w*S + S - 1 (128 rows each) and keeps their int8 A
 // fragments and the row sums of Xq (from the MFMA against ones) in registers.
-// Units (tile, step) stream through a ring of D weight loads, each column tile
-// walked front to back along K; a group's int32 sum A = raw - z * sum(Xq) is
-// exact, optionally dumped, and scaled into the fp32 partial y; per batch of T
-// tiles the 8 partial tiles are added in LDS.
+// The s and z of the workgroup's (at most T) column tiles are staged once in
+// LDS, so only the weight runs stream: units (tile, step) pass through a ring
+// of D weight loads, each column tile walked front to back along K.  A group's
+// int32 sum A = raw - z * sum(Xq) is exact, optionally dumped, and scaled into
+// the fp32 partial y; at the end the 8 partial tiles are added in LDS.
 // ---------------------------------------------------------------------------
 template <int S, int T, int D, bool PGZ>
 __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
@@ -156,7 +157,12 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                                                           uint16_t *__restrict__ Y, int32_t *__restrict__ acc_out,
                                                           int M, int K, int N, int G, int tpw)
 {
+    static_assert(S % D == 0 || D % S == 0, "ring slots must stay compile-time indexes");
     __shared__ float red[8][T][64][4];
+    // s | z << 16 of (group, column) for the workgroup's columns, group-major;
+    // the odd row stride keeps the transposing writes free of bank conflicts
+    constexpr int SZW = T * 16 + 1;
+    __shared__ uint32_t sz[64 * SZW];   // K <= 8192, G >= 128: at most 64 groups
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int m0 = blockIdx.y * 16;
@@ -164,27 +170,44 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
     const int R = K >> 5, ng = K / G, TT = R >> 2, sp = G >> 7;
     const uint32_t col_bytes = (uint32_t)R * 16u;
     const int tiles = (N + 15) >> 4;
-    const int first = blockIdx.x * tpw;
-    const int last = min(tiles, first + tpw);
+    const int tile0 = blockIdx.x * tpw;
+    const int ntile = min(tpw, tiles - tile0);   // 1 <= ntile <= T
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq, (uint32_t)((size_t)N * col_bytes));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, (uint32_t)(N * ng * 2));
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
     const int4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-    uint32_t d[D][4], sv[D], zv[D];
-    auto issue = [&](int unit, int tile0) {
-        const int slot = unit % D;
-        const int j = unit / S, st = unit % S;
+    // s and z of the workgroup's columns: wave w reads columns w, w + 8, ...,
+    // lane l holding group l (past ng, or past the workgroup's columns: zeros)
+    constexpr int SZE = T * 16 / 8;
+    uint32_t sraw[SZE], zraw[SZE];
+#pragma unroll
+    for (int e = 0; e < SZE; ++e) {
+        const int cl = wave + 8 * e;
+        const uint32_t off = (lane < ng && cl < 16 * ntile) ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)lane) * 2u : W_OOB;
+        sraw[e] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+        zraw[e] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : 0u;
+    }
+
+    // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c, run
+    // 4 t + g of step t = wave * S + st.  A step past K reads other bits of the
+    // resource (or zeros past its end) and meets zero activations; units past the
+    // workgroup's tiles load nothing.
+    uint32_t d[D][4];
+    auto issue = [&](int j, int st, int slot) {
         const int t = wave * S + st;
         const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
-        // a step past K reads other bits of the resource (or zeros past its end)
-        // and meets zero activations; the group index stays valid
-        const uint32_t grp = (uint32_t)min(t / sp, ng - 1);
-        load_dwords<LOAD_STREAM>(wr, col * col_bytes + (uint32_t)(4 * t + g) * 16u, d[slot], 4);
-        sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(sr, (col * (uint32_t)ng + grp) * 2u, 0, 0);
-        zv[slot] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, (col * (uint32_t)ng + grp) * 2u, 0, 0) : 0u;
+        load_dwords<LOAD_STREAM>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * 16u : W_OOB, d[slot], 4);
     };
+#pragma unroll
+    for (int u = 0; u < D; ++u) issue(u / S, u % S, u);
+
+#pragma unroll
+    for (int e = 0; e < SZE; ++e) {
+        const int cl = wave + 8 * e;
+        if (lane < ng) sz[lane * SZW + cl] = (sraw[e] & 0xffffu) | (zraw[e] << 16);
+    }
 
     // A fragments of step st: lane (g, c) holds row c, run 4 t + g (32 bytes), bytes
     // permuted to the nibble order of the B operand (even codes, then odd codes)
@@ -213,19 +236,23 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                                                              0, 0, 0);
         }
     }
+    __syncthreads();
 
-    for (int tile0 = first; tile0 < last; tile0 += T) {
+    // UT tiles per loop iteration keep every ring slot a compile-time index
+    constexpr int UT = D > S ? D / S : 1;
+#pragma unroll 1
+    for (int jb = 0; jb < ntile; jb += UT) {
 #pragma unroll
-        for (int u = 0; u < D && u < S * T; ++u) issue(u, tile0);
-#pragma unroll
-        for (int j = 0; j < T; ++j) {
+        for (int jj = 0; jj < UT; ++jj) {
+            const int j = jb + jj;
             float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
             int4_t graw = {0, 0, 0, 0}, gsx = {0, 0, 0, 0};
             const int n = 16 * (tile0 + j) + c;
 #pragma unroll
             for (int st = 0; st < S; ++st) {
-                const int unit = j * S + st, slot = unit % D;
+                const int slot = (jj * S + st) % D;
                 const int t = wave * S + st;
+                const uint32_t szv = sz[min(t / sp, ng - 1) * SZW + 16 * j + c];
                 int4_t raw = {0, 0, 0, 0};
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
@@ -239,16 +266,17 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                 }
                 graw += raw;
                 gsx += sxg[st];
-                const int zz = PGZ ? (int)(float)as_half((uint16_t)zv[slot]) : 8;
-                const float sc = (float)as_half((uint16_t)sv[slot]);
-                if (unit + D < S * T) issue(unit + D, tile0);
+                const int zz = PGZ ? (int)(float)as_half((uint16_t)(szv >> 16)) : 8;
+                const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
+                // refill the slot with the unit D ahead (past the tiles: no load)
+                issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
                 if ((t + 1) % sp == 0 && t < TT) {   // the group ends with this step
                     const int grp = t / sp;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int A = graw[i] - zz * gsx[i];
                         const int row = 4 * g + i;
-                        if (acc_out && row < mrows && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A;
+                        if (acc_out && row < mrows && j < ntile && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A;
                         y[i] = fmaf(sc, (float)A, y[i]);
                     }
                     graw = int4_t{0, 0, 0, 0};
@@ -258,27 +286,31 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
             // lane (g, c) of a tile holds rows 4g..4g+3, column c
             *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
         }
-        __syncthreads();
-        for (int o = threadIdx.x; o < T * 256; o += 512) {
-            const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
-            const int l = (m >> 2) * 16 + col, i = m & 3;
-            float v = 0.f;
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < ntile * 256; o += 512) {
+        const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
+        const int l = (m >> 2) * 16 + col, i = m & 3;
+        float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) v += red[w][j][l][i];
-            const int n = 16 * (tile0 + j) + col;
-            if (m < mrows && n < N && tile0 + j < last) {
-                const float sxm = (float)as_half(sx[m0 + m]);
-                Y[(size_t)(m0 + m) * N + n] = f32_to_f16_bits(sxm * v);
-            }
+        for (int w = 0; w < 8; ++w) v += red[w][j][l][i];
+        const int n = 16 * (tile0 + j) + col;
+        if (m < mrows && n < N) {
+            const float sxm = (float)as_half(sx[m0 + m]);
+            Y[(size_t)(m0 + m) * N + n] = f32_to_f16_bits(sxm * v);
         }
-        __syncthreads();
     }
 }
+
+// Weight units in flight per wave (fastest measured on the 8B MLP shape: 4
+// against 1, 2 and 8).
+constexpr int W4A8_RING = 4;
 
 template <int S, int T, bool PGZ>
 static hipError_t w4a8_stream_go(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
 {
-    constexpr int D = S * T < 8 ? S * T : 8;
+    // a power of two that divides, or is a multiple of, the steps per tile
+    constexpr int D = S * T < W4A8_RING ? S * T : W4A8_RING;
     hipLaunchKernelGGL((w4a8_stream_kernel<S, T, D, PGZ>), grid, dim3(512), 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc,
                        a.M, a.K, a.N, a.G, tpw);
     return hipGetLastError();
@@ -293,7 +325,6 @@ static hipError_t w4a8_stream_pick_t(const W4A8Args &a, dim3 grid, int tpw, hipS
     return w4a8_stream_go<S, 8, PGZ>(a, grid, tpw, st);
 }
 
-// Returns hipErrorNotSupported when the shape needs more than 8 steps per wave.
 template <bool PGZ>
 static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
 {
@@ -307,7 +338,7 @@ static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int per_m = std::max(1, cus / mtiles);
-    const int tpw = std::max(1, (tiles + per_m - 1) / per_m);
+    const int tpw = std::min(8, std::max(1, (tiles + per_m - 1) / per_m));   // one batch of tiles per workgroup
     const dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)mtiles);
     switch (S) {
         case 1: return w4a8_stream_pick_t<1, PGZ>(a, grid, tpw, st);
