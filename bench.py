@@ -18,8 +18,8 @@ kernel's algorithmic bytes (packed weights + scales + x + y) per launch
 against that mean launch duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
 prefill product (qmm_gemm) in TFLOP/s against the 2.5 PFLOP/s dense fp16 MFMA
 peak, the batched-decode (70B MLP-up shapes, M = 1, 8, 16, k = 1, 2, 5, 7, 8) and
-W4A8 (8B MLP shapes, M = 16) products as a "suite" object, and the CPU oracle
-timed on this host on a bounded sample.
+W4A8 / W8A8 (8B MLP shapes, M = 16, 4- and 8-bit weights) products as a
+"suite" object, and the CPU oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-suite]
 """
@@ -212,12 +212,13 @@ def batched_suite(torch, q, synthetic, timer, reps):
     return {"workload": w["name"], "per_bits": out}
 
 
-def w4a8_suite(torch, q, synthetic, timer, reps):
-    """8B MLP W4A8 (M 16, K 4096, N 14336, G 128): int8 activations, 4-bit weights."""
+def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
+    """8B MLP int8-activation product (M 16, K 4096, N 14336, G 128): W4A8 at
+    bits = 4 (qmm_gemm_w4a8), W8A8 at bits = 8 (qmm_gemm_wka8)."""
     w = synthetic.W4A8_8B
     M, K, N, G = w["M"], w["K"], w["N"], w["G"]
-    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(5, 4), s_range=w["s_range"])
-    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(5, bits), bits=bits, s_range=w["s_range"])
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), bits)
     bufs = rotating(torch, (wq, torch.from_numpy(c["s"]).to("cuda:0")))
     del wq
     Xq = torch.from_numpy(c["Xq"]).to("cuda:0")
@@ -228,14 +229,18 @@ def w4a8_suite(torch, q, synthetic, timer, reps):
     def launch(i):
         b = bufs[state["i"] % len(bufs)]
         state["i"] += 1
-        q.gemm_w4a8(Xq, sx, b[0], b[1], None, G, out=y)
+        if bits == 4:
+            q.gemm_w4a8(Xq, sx, b[0], b[1], None, G, out=y)
+        else:
+            q.gemm_wka8(Xq, sx, b[0], b[1], None, bits, G, out=y)
 
     for i in range(3):
         launch(i)
     ms = timer.region_ms(launch, reps) / reps
-    wq_bytes = N * K // 2
+    wq_bytes = N * K * bits // 8
     alg = wq_bytes + N * (K // G) * 2 + M * K + M * 2 + M * N * 2
-    return {"workload": w["name"], "us": round(ms * 1e3, 2), "packed_GBs": round(wq_bytes / ms / 1e6, 1),
+    name = w["name"] if bits == 4 else w["name"].replace("w4a8", f"w{bits}a8").replace(" k4 ", f" k{bits} ")
+    return {"workload": name, "us": round(ms * 1e3, 2), "packed_GBs": round(wq_bytes / ms / 1e6, 1),
             "algorithmic_GBs": round(alg / ms / 1e6, 1),
             "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
@@ -321,10 +326,11 @@ def main():
 
     suite = None
     if not args.no_suite:
-        print("bench: timing the batched-decode and W4A8 workloads", file=sys.stderr, flush=True)
+        print("bench: timing the batched-decode and int8-activation workloads", file=sys.stderr, flush=True)
         reps = max(10, args.steps // 2)
         suite = {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
-                 "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps)}
+                 "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
+                 "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8)}
 
     cpu = None
     if not args.no_cpu:

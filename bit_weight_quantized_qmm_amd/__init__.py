@@ -18,9 +18,10 @@ import torch
 
 from ._build import LIBRARY
 
-__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "library_path", "SYMBOLS"]
+__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "library_path",
+           "SYMBOLS"]
 
-SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8",
+SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8",
            "qmm_status_string", "qmm_last_error")
 
 
@@ -42,6 +43,7 @@ def _load():
         "qmm_gemv": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm_w4a8": ([P, P, P, P, P, P, P, I64, I64, I64, I64, P], INT),
+        "qmm_gemm_wka8": ([P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_status_string": ([INT], ctypes.c_char_p),
         "qmm_last_error": ([], ctypes.c_char_p),
     }
@@ -138,11 +140,20 @@ def gemm(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
 def gemm_w4a8(Xq, sx, wq, s, z, G: int, out=None, acc_out=None) -> torch.Tensor:
     """Y [M, N] fp16 for int8 activations Xq [M, K] with per-token fp16 scales sx [M] and
     4-bit weights; acc_out (int32 [M, K/G, N]) optionally receives the exact group sums."""
+    return _int8_product(False, Xq, sx, wq, s, z, 4, G, out, acc_out)
+
+
+def gemm_wka8(Xq, sx, wq, s, z, bits: int, G: int, out=None, acc_out=None) -> torch.Tensor:
+    """As gemm_w4a8 for bits-bit weights, bits in 1..8 (8: W8A8)."""
+    return _int8_product(True, Xq, sx, wq, s, z, bits, G, out, acc_out)
+
+
+def _int8_product(any_bits: bool, Xq, sx, wq, s, z, bits: int, G: int, out, acc_out) -> torch.Tensor:
     _need(Xq, "Xq", torch.int8)
     M, K = Xq.shape
     N = s.shape[0]
     _need(sx, "sx", torch.float16, (M,), Xq.device)
-    _need(wq, "wq", torch.int32, (N, K * 4 // 32), Xq.device)
+    _need(wq, "wq", torch.int32, (N, K * bits // 32), Xq.device)
     _need(s, "s", torch.float16, (N, K // G), Xq.device)
     if z is not None:
         _need(z, "z", torch.float16, (N, K // G), Xq.device)
@@ -151,6 +162,9 @@ def gemm_w4a8(Xq, sx, wq, s, z, G: int, out=None, acc_out=None) -> torch.Tensor:
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
     _need(out, "out", torch.float16, (M, N), Xq.device)
-    _check(_lib.qmm_gemm_w4a8(_ptr(Xq), _ptr(sx), _ptr(wq), _ptr(s), _ptr(z), _ptr(out), _ptr(acc_out),
-                              M, K, N, G, _stream(Xq.device)))
+    ptrs = (_ptr(Xq), _ptr(sx), _ptr(wq), _ptr(s), _ptr(z), _ptr(out), _ptr(acc_out))
+    if any_bits:
+        _check(_lib.qmm_gemm_wka8(*ptrs, M, K, N, bits, G, _stream(Xq.device)))
+    else:
+        _check(_lib.qmm_gemm_w4a8(*ptrs, M, K, N, G, _stream(Xq.device)))
     return out

@@ -104,12 +104,11 @@ qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
     return product("qmm_gemm", false, X, wq, s, z, Y, M, K, N, bits, G, stream);
 }
 
-qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
-                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K, int64_t N,
-                         int64_t G, qmm_stream stream)
+static qmm_status int8_product(const char *fn, const int8_t *Xq, const qmm_half *sx, const uint32_t *wq,
+                               const qmm_half *s, const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M,
+                               int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)
 {
-    const char *fn = "qmm_gemm_w4a8";
-    qmm_status st = check_shape(fn, M, K, N, 4, G, true);
+    qmm_status st = check_shape(fn, M, K, N, bits, G, true);
     if (st != QMM_OK) return st;
     if (!Xq || !sx || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
     if (G % 128 != 0 || (G / 128 & (G / 128 - 1)) != 0 || G > 1024)
@@ -117,8 +116,22 @@ qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *w
     if ((M + 15) / 16 > 65535) return fail(QMM_ERR_UNSUPPORTED, "%s: M too large", fn);
     if (acc_out && M * (K / G) * N > (int64_t(1) << 31) - 1)
         return fail(QMM_ERR_UNSUPPORTED, "%s: accumulator dump too large", fn);
-    qmm::W4A8Args a{Xq, sx, wq, s, z, Y, acc_out, (int)M, (int)K, (int)N, (int)G};
+    qmm::W4A8Args a{Xq, sx, wq, s, z, Y, acc_out, (int)M, (int)K, (int)N, bits, (int)G};
     return hip_status(qmm::launch_w4a8(a, (hipStream_t)stream), fn);
+}
+
+qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
+                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K, int64_t N,
+                         int64_t G, qmm_stream stream)
+{
+    return int8_product("qmm_gemm_w4a8", Xq, sx, wq, s, z, Y, acc_out, M, K, N, 4, G, stream);
+}
+
+qmm_status qmm_gemm_wka8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
+                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K, int64_t N, int bits,
+                         int64_t G, qmm_stream stream)
+{
+    return int8_product("qmm_gemm_wka8", Xq, sx, wq, s, z, Y, acc_out, M, K, N, bits, G, stream);
 }
 
 const char *qmm_status_string(qmm_status status)

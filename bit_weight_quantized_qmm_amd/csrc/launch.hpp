@@ -18,12 +18,12 @@ struct GemvArgs {
 struct W4A8Args {
     const int8_t *Xq;      // [M][K]
     const uint16_t *sx;    // fp16 [M]
-    const uint32_t *wq;    // [N][K/8]
+    const uint32_t *wq;    // [N][K*bits/32]
     const uint16_t *s;     // fp16 [N][K/G]
     const uint16_t *z;     // fp16 [N][K/G] or nullptr
     uint16_t *Y;           // fp16 [M][N]
     int32_t *acc;          // int32 [M][K/G][N] or nullptr
-    int M, K, N, G;
+    int M, K, N, bits, G;
 };
 
 hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, hipStream_t st);

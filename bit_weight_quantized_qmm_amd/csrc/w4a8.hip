@@ -1,4 +1,5 @@
-// w4a8.hip -- int8 activations x 4-bit weights with exact int32 group sums.
+// w4a8.hip -- int8 activations x k-bit weights (k = 1..8) with exact int32
+// group sums.
 //
 // BitLLM Sec. 4.3 defines the integer dot product (dp4a: products of 8-bit
 // values summed exactly into an int32) and Sec. 4.4 keeps the whole hot loop in
@@ -7,9 +8,12 @@
 // quantisation group:
 //   A[m][g][n] = sum_{i in g} Xq[m][i] * q[i][n]  -  z[n][g] * sum_{i in g} Xq[m][i]
 //   y[m][n]   += s[n][g] * float(A[m][g][n]),          Y = fp16(sx[m] * y)
-// 4-bit codes become int8 lanes with one AND (even nibbles) and one shift+AND
-// (odd nibbles) per dword; Xq is permuted once into that byte order.  The
-// per-row group sums of Xq come from the same MFMA against an all-ones B.
+// A lane's run of 32 codes becomes 32 int8 lanes (wka8_dword): for k = 1, 2, 4
+// one shift and one AND per output dword, for k = 8 the bytes themselves with
+// the sign bit flipped (q - 128, the zero point shifted to match), for the odd
+// widths one bit-field extract per code.  Xq is permuted once into the same
+// byte order.  The per-row group sums of Xq come from the same MFMA against an
+// all-ones B.
 //
 // Workgroup: 8 waves split K for one 16-column x 16-row tile; a K step is 128
 // rows = 4 runs, lane group g owning run 4t+g.  Requires G % 128 == 0 so that
@@ -23,7 +27,71 @@ namespace qmm {
 
 constexpr uint32_t W_OOB = 0x80000000u;
 
-template <int T, bool PGZ>
+// Byte b of dword o (o = 0..7) of a run's int8 form holds code wka8_code(o, b)
+// of the run.  For k = 1, 2, 4 (C = 32 / k codes per dword, P = C / 4 output
+// dwords per input dword) output dword o is input dword o / P shifted right by
+// k (o % P) and masked to the low k bits of every byte; k = 8 and the odd
+// widths keep the codes in order.
+template <int BITS>
+__host__ __device__ constexpr int wka8_code(int o, int b)
+{
+    return (BITS == 1 || BITS == 2 || BITS == 4) ? (32 / BITS) * (o / (8 / BITS)) + (8 / BITS) * b + o % (8 / BITS)
+                                                 : 4 * o + b;
+}
+
+// Output dword o of the int8 form of a run of BITS dwords (o a compile-time
+// constant after unrolling).  For k = 8 the byte is q - 128: a signed byte.
+template <int BITS>
+__device__ __forceinline__ uint32_t wka8_dword(const uint32_t (&d)[BITS], int o)
+{
+    if constexpr (BITS == 8) {
+        return d[o] ^ 0x80808080u;
+    } else if constexpr (BITS == 1 || BITS == 2 || BITS == 4) {
+        constexpr int P = 8 / BITS;
+        constexpr uint32_t mask = ((1u << BITS) - 1u) * 0x01010101u;
+        return (d[o / P] >> (BITS * (o % P))) & mask;
+    } else {
+        uint32_t r = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int bit = (4 * o + b) * BITS, w = bit >> 5, sh = bit & 31;
+            const uint32_t v = sh + BITS <= 32 ? (d[w] >> sh) : __builtin_amdgcn_alignbit(d[w + 1], d[w], sh);
+            r |= (v & ((1u << BITS) - 1u)) << (8 * b);
+        }
+        return r;
+    }
+}
+
+// Dword o of a row's 32 activation bytes x[0..7] in the same order.
+template <int BITS>
+__device__ __forceinline__ uint32_t wka8_xdword(const uint32_t (&x)[8], int o)
+{
+    if constexpr (BITS == 4) {
+        // bytes 0, 2, 4, 6 (o even) or 1, 3, 5, 7 (o odd) of x[o & ~1], x[o | 1]
+        return __builtin_amdgcn_perm(x[o | 1], x[o & ~1], (o & 1) ? 0x07050301u : 0x06040200u);
+    } else if constexpr (BITS == 8 || !(BITS == 1 || BITS == 2)) {
+        return x[o];
+    } else {
+        uint32_t r = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = wka8_code<BITS>(o, b);
+            r |= ((x[i >> 2] >> (8 * (i & 3))) & 0xffu) << (8 * b);
+        }
+        return r;
+    }
+}
+
+// Zero point as the integer the int8 B operand needs: z for k < 8, z - 128
+// for k = 8 (whose B bytes are q - 128); the default z is 2^(k-1).
+template <int BITS, bool PGZ>
+__device__ __forceinline__ int wka8_zero(uint32_t zbits)
+{
+    const int zq = PGZ ? (int)(float)as_half((uint16_t)zbits) : (1 << (BITS - 1));
+    return BITS == 8 ? zq - 128 : zq;
+}
+
+template <int BITS, int T, bool PGZ>
 __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
                                                    const uint32_t *__restrict__ wq, const uint16_t *__restrict__ s,
                                                    const uint16_t *__restrict__ z, uint16_t *__restrict__ Y,
@@ -35,7 +103,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
     const int g = lane >> 4, c = lane & 15;
     const int m0 = blockIdx.y * 16;
     const int R = K >> 5, ng = K / G, steps_per_group = G / 128;
-    const uint32_t col_bytes = (uint32_t)R * 16u;
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int mrows = min(16, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
     const int tiles = (N + 15) >> 4;
@@ -47,21 +115,21 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
     for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
         const int n = tile * 16 + c;
         const int nvalid = min(16, N - tile * 16);
-        const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)tile * 16 * R * 4, (uint32_t)nvalid * col_bytes);
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)tile * 16 * R * BITS, (uint32_t)nvalid * col_bytes);
         const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)tile * 16 * ng, (uint32_t)(nvalid * ng * 2));
         const __amdgpu_buffer_rsrc_t zr =
             make_rsrc(PGZ ? z + (size_t)tile * 16 * ng : s, PGZ ? (uint32_t)(nvalid * ng * 2) : 0u);
         float y[4] = {0.f, 0.f, 0.f, 0.f};
         for (int pass = 0; pass < passes; ++pass) {
             const int tt0 = pass * 8 * T + wave * T;
-            uint32_t d[T][4];
+            uint32_t d[T][BITS];
             uint16_t sv[T], zv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const int tt = tt0 + t;
                 const int run = 4 * tt + g;
-                const uint32_t off = (run < R) ? (uint32_t)c * col_bytes + (uint32_t)run * 16u : W_OOB;
-                load_dwords<LOAD_STREAM>(wr, off, d[t], 4);
+                const uint32_t off = (run < R) ? (uint32_t)c * col_bytes + (uint32_t)run * run_bytes : W_OOB;
+                load_dwords<LOAD_STREAM>(wr, off, d[t], BITS);
                 const uint32_t soff = (4 * tt < R) ? (uint32_t)(c * ng + (tt * 128) / G) * 2u : W_OOB;
                 sv[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
                 zv[t] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, soff, 0, 0) : (uint16_t)0;
@@ -74,14 +142,9 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
                     const uint32_t off = (run < R) ? (uint32_t)c * K + (uint32_t)run * 32u : W_OOB;
                     load_dwords<LOAD_DEFAULT>(xr, off, x, 8);
 #pragma unroll
-                    for (int v = 0; v < 2; ++v) {
-                        int4_t av;
-                        av[0] = (int)__builtin_amdgcn_perm(x[4 * v + 1], x[4 * v], 0x06040200u);
-                        av[1] = (int)__builtin_amdgcn_perm(x[4 * v + 1], x[4 * v], 0x07050301u);
-                        av[2] = (int)__builtin_amdgcn_perm(x[4 * v + 3], x[4 * v + 2], 0x06040200u);
-                        av[3] = (int)__builtin_amdgcn_perm(x[4 * v + 3], x[4 * v + 2], 0x07050301u);
-                        a[t][v] = av;
-                    }
+                    for (int v = 0; v < 2; ++v)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[t][v][e] = (int)wka8_xdword<BITS>(x, 4 * v + e);
                     int4_t zero4 = {0, 0, 0, 0};
                     int4_t sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][0], ones, zero4, 0, 0, 0);
                     sxg[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][1], ones, sum, 0, 0, 0);
@@ -95,19 +158,16 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
                 int4_t raw = {0, 0, 0, 0};
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
-                    const uint32_t da = d[t][2 * v], db = d[t][2 * v + 1];
                     int4_t bv;
-                    bv[0] = (int)(da & 0x0f0f0f0fu);
-                    bv[1] = (int)((da >> 4) & 0x0f0f0f0fu);
-                    bv[2] = (int)(db & 0x0f0f0f0fu);
-                    bv[3] = (int)((db >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = (int)wka8_dword<BITS>(d[t], 4 * v + e);
                     raw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][v], bv, raw, 0, 0, 0);
                 }
                 graw += raw;
                 gsx += sxg[t];
                 if ((tt + 1) % steps_per_group == 0 || 4 * (tt + 1) >= R) {
                     const int grp = (tt * 128) / G;
-                    const int zz = PGZ ? (int)(float)as_half(zv[t]) : 8;
+                    const int zz = wka8_zero<BITS, PGZ>(zv[t]);
                     const float sc = (float)as_half(sv[t]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -150,7 +210,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
 // int32 sum A = raw - z * sum(Xq) is exact, optionally dumped, and scaled into
 // the fp32 partial y; at the end the 8 partial tiles are added in LDS.
 // ---------------------------------------------------------------------------
-template <int S, int T, int D, bool PGZ>
+template <int BITS, int S, int T, int D, bool PGZ>
 __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
                                                           const uint32_t *__restrict__ wq,
                                                           const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
@@ -168,7 +228,7 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
     const int m0 = blockIdx.y * 16;
     const int mrows = min(16, M - m0);
     const int R = K >> 5, ng = K / G, TT = R >> 2, sp = G >> 7;
-    const uint32_t col_bytes = (uint32_t)R * 16u;
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int tiles = (N + 15) >> 4;
     const int tile0 = blockIdx.x * tpw;
     const int ntile = min(tpw, tiles - tile0);   // 1 <= ntile <= T
@@ -194,11 +254,11 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
     // 4 t + g of step t = wave * S + st.  A step past K reads other bits of the
     // resource (or zeros past its end) and meets zero activations; units past the
     // workgroup's tiles load nothing.
-    uint32_t d[D][4];
+    uint32_t d[D][BITS];
     auto issue = [&](int j, int st, int slot) {
         const int t = wave * S + st;
         const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
-        load_dwords<LOAD_STREAM>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * 16u : W_OOB, d[slot], 4);
+        load_dwords<LOAD_STREAM>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * run_bytes : W_OOB, d[slot], BITS);
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(u / S, u % S, u);
@@ -222,14 +282,9 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
 #pragma unroll
         for (int st = 0; st < S; ++st) {
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                int4_t av;
-                av[0] = (int)__builtin_amdgcn_perm(x[st][4 * v + 1], x[st][4 * v], 0x06040200u);
-                av[1] = (int)__builtin_amdgcn_perm(x[st][4 * v + 1], x[st][4 * v], 0x07050301u);
-                av[2] = (int)__builtin_amdgcn_perm(x[st][4 * v + 3], x[st][4 * v + 2], 0x06040200u);
-                av[3] = (int)__builtin_amdgcn_perm(x[st][4 * v + 3], x[st][4 * v + 2], 0x07050301u);
-                a[st][v] = av;
-            }
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[st][v][e] = (int)wka8_xdword<BITS>(x[st], 4 * v + e);
             const int4_t zero4 = {0, 0, 0, 0};
             sxg[st] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][1], ones,
                                                              __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][0], ones, zero4, 0, 0, 0),
@@ -256,17 +311,14 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                 int4_t raw = {0, 0, 0, 0};
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
-                    const uint32_t da = d[slot][2 * v], db = d[slot][2 * v + 1];
                     int4_t bv;
-                    bv[0] = (int)(da & 0x0f0f0f0fu);
-                    bv[1] = (int)((da >> 4) & 0x0f0f0f0fu);
-                    bv[2] = (int)(db & 0x0f0f0f0fu);
-                    bv[3] = (int)((db >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = (int)wka8_dword<BITS>(d[slot], 4 * v + e);
                     raw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][v], bv, raw, 0, 0, 0);
                 }
                 graw += raw;
                 gsx += sxg[st];
-                const int zz = PGZ ? (int)(float)as_half((uint16_t)(szv >> 16)) : 8;
+                const int zz = wka8_zero<BITS, PGZ>(szv >> 16);
                 const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
                 // refill the slot with the unit D ahead (past the tiles: no load)
                 issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
@@ -302,30 +354,31 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
     }
 }
 
-// Weight units in flight per wave (fastest measured on the 8B MLP shape: 4
-// against 1, 2 and 8).
+// Weight units in flight per wave (fastest measured on the 8B MLP shape at
+// k = 4: 4 against 1, 2 and 8).
 constexpr int W4A8_RING = 4;
 
-template <int S, int T, bool PGZ>
+template <int BITS, int S, int T, bool PGZ>
 static hipError_t w4a8_stream_go(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
 {
     // a power of two that divides, or is a multiple of, the steps per tile
     constexpr int D = S * T < W4A8_RING ? S * T : W4A8_RING;
-    hipLaunchKernelGGL((w4a8_stream_kernel<S, T, D, PGZ>), grid, dim3(512), 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc,
-                       a.M, a.K, a.N, a.G, tpw);
+    hipLaunchKernelGGL((w4a8_stream_kernel<BITS, S, T, D, PGZ>), grid, dim3(512), 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y,
+                       a.acc, a.M, a.K, a.N, a.G, tpw);
     return hipGetLastError();
 }
 
-template <int S, bool PGZ>
+template <int BITS, int S, bool PGZ>
 static hipError_t w4a8_stream_pick_t(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
 {
-    if (tpw <= 1) return w4a8_stream_go<S, 1, PGZ>(a, grid, tpw, st);
-    if (tpw <= 2) return w4a8_stream_go<S, 2, PGZ>(a, grid, tpw, st);
-    if (tpw <= 4) return w4a8_stream_go<S, 4, PGZ>(a, grid, tpw, st);
-    return w4a8_stream_go<S, 8, PGZ>(a, grid, tpw, st);
+    if (tpw <= 1) return w4a8_stream_go<BITS, S, 1, PGZ>(a, grid, tpw, st);
+    if (tpw <= 2) return w4a8_stream_go<BITS, S, 2, PGZ>(a, grid, tpw, st);
+    if (tpw <= 4) return w4a8_stream_go<BITS, S, 4, PGZ>(a, grid, tpw, st);
+    return w4a8_stream_go<BITS, S, 8, PGZ>(a, grid, tpw, st);
 }
 
-template <bool PGZ>
+// Returns hipErrorNotSupported when the shape needs more than 8 steps per wave.
+template <int BITS, bool PGZ>
 static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
 {
     const int TT = a.K / 128, sp = a.G / 128;
@@ -341,19 +394,19 @@ static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
     const int tpw = std::min(8, std::max(1, (tiles + per_m - 1) / per_m));   // one batch of tiles per workgroup
     const dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)mtiles);
     switch (S) {
-        case 1: return w4a8_stream_pick_t<1, PGZ>(a, grid, tpw, st);
-        case 2: return w4a8_stream_pick_t<2, PGZ>(a, grid, tpw, st);
-        case 4: return w4a8_stream_pick_t<4, PGZ>(a, grid, tpw, st);
-        default: return w4a8_stream_pick_t<8, PGZ>(a, grid, tpw, st);
+        case 1: return w4a8_stream_pick_t<BITS, 1, PGZ>(a, grid, tpw, st);
+        case 2: return w4a8_stream_pick_t<BITS, 2, PGZ>(a, grid, tpw, st);
+        case 4: return w4a8_stream_pick_t<BITS, 4, PGZ>(a, grid, tpw, st);
+        default: return w4a8_stream_pick_t<BITS, 8, PGZ>(a, grid, tpw, st);
     }
 }
 
-template <bool PGZ>
+template <int BITS, bool PGZ>
 static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipStream_t st)
 {
     const dim3 block(512);
-#define QMM_W(TV)                                                                                            \
-    hipLaunchKernelGGL((w4a8_kernel<TV, PGZ>), grid, block, 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc, a.M, \
+#define QMM_W(TV)                                                                                                  \
+    hipLaunchKernelGGL((w4a8_kernel<BITS, TV, PGZ>), grid, block, 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc, a.M, \
                        a.K, a.N, a.G, passes)
     switch (T) {
         case 1: QMM_W(1); break;
@@ -366,12 +419,11 @@ static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipSt
     return hipGetLastError();
 }
 
-// Returns hipErrorNotSupported for shapes this kernel does not cover.
-hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st)
+template <int BITS>
+static hipError_t launch_wka8_bits(const W4A8Args &a, hipStream_t st)
 {
-    if (a.G % 128 != 0 || a.G > 1024) return hipErrorNotSupported;
-    if (a.K <= 8192 && (size_t)a.N * (a.K / 32) * 16 < 0x7fffffffu) {
-        const hipError_t e = a.z ? w4a8_stream_launch<true>(a, st) : w4a8_stream_launch<false>(a, st);
+    if (a.K <= 8192 && (size_t)a.N * (a.K / 32) * 4 * BITS < 0x7fffffffu) {
+        const hipError_t e = a.z ? w4a8_stream_launch<BITS, true>(a, st) : w4a8_stream_launch<BITS, false>(a, st);
         if (e != hipErrorNotSupported) return e;
     }
     const int R = a.K / 32;
@@ -384,7 +436,24 @@ hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st)
     const int mtiles = (a.M + 15) / 16;
     if (mtiles > 65535) return hipErrorNotSupported;
     const dim3 grid((unsigned)min(tiles, 512), (unsigned)mtiles);
-    return a.z ? w4a8_go<true>(a, T, passes, grid, st) : w4a8_go<false>(a, T, passes, grid, st);
+    return a.z ? w4a8_go<BITS, true>(a, T, passes, grid, st) : w4a8_go<BITS, false>(a, T, passes, grid, st);
+}
+
+// Returns hipErrorNotSupported for shapes these kernels do not cover.
+hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st)
+{
+    if (a.G % 128 != 0 || a.G > 1024) return hipErrorNotSupported;
+    switch (a.bits) {
+        case 1: return launch_wka8_bits<1>(a, st);
+        case 2: return launch_wka8_bits<2>(a, st);
+        case 3: return launch_wka8_bits<3>(a, st);
+        case 4: return launch_wka8_bits<4>(a, st);
+        case 5: return launch_wka8_bits<5>(a, st);
+        case 6: return launch_wka8_bits<6>(a, st);
+        case 7: return launch_wka8_bits<7>(a, st);
+        case 8: return launch_wka8_bits<8>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qmm

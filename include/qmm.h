@@ -123,6 +123,22 @@ qmm_status qmm_gemm_w4a8(const int8_t *Xq, const qmm_half *sx, const uint32_t *w
                          const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K,
                          int64_t N, int64_t G, qmm_stream stream);
 
+/* The integer-activation product of qmm_gemm_w4a8 for any code width
+ * bits = 1..8 (bits = 8 is the W8A8 setting and bits = 4 the W4A8 setting
+ * that BitLLM Sec. 5.1 evaluates, both with group-wise scales):
+ *   A[m][g][n] = sum_{i in group g} Xq[m][i] * (q[i][n] - z[n][g])   (exact int32)
+ *   Y[m][n]    = fp16( sx[m] * sum_g s[n][g] * A[m][g][n] )          (fp32)
+ * wq is the packed stream of qmm_pack for the same bits ([N][K*bits/32]); z
+ * must be integer-valued in [0, 2^bits - 1] (NULL = 2^(bits-1)).  Each lane's
+ * run of 32 codes becomes 32 int8 MFMA lanes in registers; for bits = 8 the
+ * bytes enter as q - 128 and the zero-point as z - 128, which leaves A
+ * unchanged.  Every other argument, the layouts, the ownership (all device
+ * pointers, nothing retained) and the error behaviour are those of
+ * qmm_gemm_w4a8; bits outside 1..8 give QMM_ERR_INVALID_ARG. */
+qmm_status qmm_gemm_wka8(const int8_t *Xq, const qmm_half *sx, const uint32_t *wq, const qmm_half *s,
+                         const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K,
+                         int64_t N, int bits, int64_t G, qmm_stream stream);
+
 /* Static text for a status code. */
 const char *qmm_status_string(qmm_status status);
 

@@ -233,6 +233,38 @@ def pin_w4a8_bruteforce(orc):
                 assert abs(Fraction(Y[m, n]) - Yx[m][n]) <= bound, (m, n)
 
 
+def pin_wka8_every_width_bruteforce(orc):
+    """The integer product for every code width: A bit-exact vs Python integers
+    (codes at both ends of their range included), Y within the fp64 bound."""
+    for bits in range(1, 9):
+        M, K, N, G = 2, 64, 3, 32
+        pgz = bits % 2 == 1
+        c = synthetic.make_w4a8_case(M, K, N, G, 1600 + bits, bits=bits, per_group_z=pgz)
+        c["codes"][:, 0] = (1 << bits) - 1
+        c["codes"][:, 1] = 0
+        st = brute.bigint_pack(c["codes"], bits)
+        A, Y = orc.w4a8(c["Xq"], c["sx"], st, c["s"], c["z"], G, bits=bits)
+        Ax, Yx = brute.exact_w4a8(c["Xq"], c["sx"], c["codes"], c["s"], c["z"], bits, G)
+        assert np.array_equal(A, Ax), bits
+        ng = K // G
+        for m in range(M):
+            for n in range(N):
+                terms = sum(abs(brute.frac(c["s"][n, g]) * int(Ax[m, g, n])) for g in range(ng))
+                bound = brute.frac(c["sx"][m]) * terms * Fraction(2.0 ** -52 * (ng + 2)) + Fraction(1, 10 ** 300)
+                assert abs(Fraction(Y[m, n]) - Yx[m][n]) <= bound, (bits, m, n)
+
+
+def pin_w8a8_matches_integer_matmul(orc):
+    """k = 8 with the default zero-point 128: per group A = Xq[:, g] @ (Q[g] - 128)."""
+    M, K, N, G = 3, 256, 5, 128
+    c = synthetic.make_w4a8_case(M, K, N, G, 1700, bits=8)
+    st = brute.bigint_pack(c["codes"], 8)
+    A, _ = orc.w4a8(c["Xq"], c["sx"], st, c["s"], None, G, bits=8)
+    Q = c["codes"].astype(np.int64) - 128
+    for g in range(K // G):
+        assert np.array_equal(A[:, g, :], c["Xq"][:, g * G:(g + 1) * G].astype(np.int64) @ Q[g * G:(g + 1) * G])
+
+
 def pin_w4a8_matches_integer_matmul(orc):
     """Per group, A = Xq[:, g] @ (Q[g] - z): numpy int64 matmul as the library special case."""
     M, K, N, G = 4, 256, 6, 128

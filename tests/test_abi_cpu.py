@@ -36,6 +36,8 @@ def lib():
         getattr(lib, f).restype = INT
     lib.qmm_gemm_w4a8.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.qmm_gemm_w4a8.restype = INT
+    lib.qmm_gemm_wka8.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P]
+    lib.qmm_gemm_wka8.restype = INT
     lib.qmm_status_string.argtypes = [INT]
     lib.qmm_status_string.restype = ctypes.c_char_p
     lib.qmm_last_error.restype = ctypes.c_char_p
@@ -44,7 +46,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
-    for name in ("qmm_pack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8"):
+    for name in ("qmm_pack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8"):
         assert name in syms
 
 
@@ -117,6 +119,18 @@ def test_w4a8_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 64, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 384, None) in (INVALID, UNSUPPORTED)
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, 4096, 64, 128, None) == INVALID
+
+
+def test_wka8_validation(lib):
+    """Host-side checks only (every call returns before any HIP call)."""
+    f = lib.qmm_gemm_wka8
+    for bits in (0, 9, -1):
+        assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, bits, 128, None) == INVALID
+    assert f(None, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 8, 128, None) == INVALID
+    assert f(FAKE, FAKE, None, FAKE, None, FAKE, None, 16, 4096, 64, 8, 128, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 8, 64, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 3, 2048, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4000, 64, 8, 128, None) == INVALID
 
 
 def test_status_strings(lib):

@@ -316,3 +316,83 @@ def test_w4a8_workload(q, orc):
     assert rel_err(Y, ref) <= TOL
     Y2, _ = run_w4a8(q, c, with_acc=False)
     assert torch.equal(Y.cpu(), Y2.cpu())
+
+
+# ------------------------------------------------- WkA8 (any code width) ---
+def run_wka8(q, c, bits, with_acc=True):
+    wq = gpu_pack(q, c["codes"], bits)
+    M, K = c["Xq"].shape
+    N = c["codes"].shape[1]
+    acc = torch.full((M, K // c["G"], N), -12345, dtype=torch.int32, device=DEV) if with_acc else None
+    z = None if c["z"] is None else dev(c["z"])
+    Y = q.gemm_wka8(dev(c["Xq"]), dev(c["sx"]), wq, dev(c["s"]), z, bits, c["G"], acc_out=acc)
+    return Y, acc
+
+
+def check_wka8(orc, c, bits, Y, acc):
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], bits), c["s"], c["z"], c["G"], bits=bits)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("M", [1, 5, 17])
+@pytest.mark.parametrize("G,pgz", [(128, False), (256, True)])
+def test_wka8_small(q, orc, bits, M, G, pgz):
+    """Every code width through the streaming kernel: several column tiles, a
+    ragged column tail and a ragged M tile."""
+    K, N = 1024, 70
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(97, bits, M + G), bits=bits, per_group_z=pgz)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+
+
+@pytest.mark.parametrize("bits,M,K,N,G,pgz", [(8, 3, 2048, 50, 512, True), (3, 16, 2048, 33, 1024, False),
+                                               (7, 8, 8192, 40, 128, True), (1, 2, 16384, 20, 256, False),
+                                               (5, 40, 3072, 65, 128, True), (6, 4, 16384, 24, 128, True),
+                                               (2, 9, 4096, 300, 128, False)])
+def test_wka8_shapes(q, orc, bits, M, K, N, G, pgz):
+    """Groups spanning several steps, K slices that leave waves idle, and K past
+    the streaming kernel's register slice (the tiled kernel)."""
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(98, bits, M), bits=bits, per_group_z=pgz)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+
+
+@pytest.mark.parametrize("bits", [2, 5, 8])
+@pytest.mark.parametrize("K,G", [(512, 128), (16384, 1024)])
+def test_wka8_extreme(q, orc, bits, K, G):
+    """-128 activations against the largest and smallest codes with zero-points
+    at both ends: the int32 sums reach their largest magnitudes and stay exact."""
+    M, N = 16, 40
+    c = synthetic.make_w4a8_case(M, K, N, G, 12 + bits, bits=bits, per_group_z=True)
+    c["Xq"][:] = -128
+    c["codes"][:, ::2] = (1 << bits) - 1
+    c["codes"][:, 1::2] = 0
+    c["z"][::2, :] = 0
+    c["z"][1::2, :] = (1 << bits) - 1
+    # scale s by a power of two (exact; A does not depend on s) so that Y stays
+    # inside the fp16 range
+    _, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], bits), c["s"], c["z"], G, bits=bits)
+    e = max(0, int(np.ceil(np.log2(np.abs(ref).max() / 16384.0))))
+    c["s"] = (c["s"].astype(np.float32) / (1 << e)).astype(np.float16)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+
+
+def test_wka8_four_bits_is_w4a8(q):
+    """The general entry point at k = 4 is the W4A8 product, bit for bit."""
+    c = synthetic.make_w4a8_case(16, 2048, 100, 128, 31, per_group_z=True)
+    Y4, acc4 = run_w4a8(q, c)
+    Yk, acck = run_wka8(q, c, 4)
+    assert torch.equal(Y4.cpu(), Yk.cpu()) and torch.equal(acc4.cpu(), acck.cpu())
+
+
+def test_w8a8_workload(q, orc):
+    """The 8B MLP shape with 8-bit weights (the W8A8 setting), checked whole."""
+    w = synthetic.W4A8_8B
+    c = synthetic.make_w4a8_case(w["M"], w["K"], w["N"], w["G"], synthetic.seed_for(5, 8), bits=8)
+    Y, acc = run_wka8(q, c, 8)
+    check_wka8(orc, c, 8, Y, acc)
+    Y2, _ = run_wka8(q, c, 8, with_acc=False)
+    assert torch.equal(Y.cpu(), Y2.cpu())
