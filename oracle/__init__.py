@@ -63,6 +63,7 @@ class Oracle:
             "qmm_oracle_qmm": [_P, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P],
             "qmm_oracle_qmm_sampled": [_P, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P, _P, _I64, _P],
             "qmm_oracle_w4a8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P, _P],
+            "qmm_oracle_quantize": [_P, _I64, _I64, _INT, _I64, _P, _P, _P],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -153,6 +154,18 @@ class Oracle:
                                       _ptr(A), _ptr(Y))
         self._check(rc, "w4a8")
         return A, Y
+
+
+    def quantize(self, W, bits: int, G: int):
+        """(codes uint8 [K][N], s float16 [N][K/G], z float16 [N][K/G]) for fp16 W [K][N]."""
+        W64 = np.ascontiguousarray(np.asarray(W, dtype=np.float16).astype(np.float64))
+        K, N = W64.shape
+        codes = np.zeros((K, N), dtype=np.uint8)
+        s = np.zeros((N, K // G), dtype=np.float64)
+        z = np.zeros((N, K // G), dtype=np.float64)
+        self._check(self.lib.qmm_oracle_quantize(_ptr(W64), K, N, bits, G, _ptr(codes), _ptr(s), _ptr(z)),
+                    "quantize")
+        return codes, s.astype(np.float16), z.astype(np.float16)
 
 
 _default: Oracle | None = None

@@ -38,6 +38,10 @@
  * widened exactly by the caller); z == NULL means z = 2^(k-1).  Group g of a
  * column covers rows [g*G, (g+1)*G).
  *
+ * The quantiser (qmm_oracle_quantize) follows eq. (1) of the same section,
+ * q = clip(round(w / s) + z, 0, 2^k - 1), with s and z chosen per (column,
+ * group) from the group's range; its header states the reading.
+ *
  * Status: 0 = ok, -1 = invalid shape or argument, -2 = non-integer zero-point
  * where the integer path needs one, -3 = int32 accumulator range exceeded.
  */
@@ -226,4 +230,62 @@ int qmm_oracle_w4a8(const int8_t *Xq, const double *sx, const uint8_t *stream,
     }
     if (failed) return -1;
     return overflow ? -3 : 0;
+}
+
+/* Nearest fp16 value to x >= 0 (ties to even significand), as a double; +inf
+ * past the largest finite fp16 value.  fp16 values in [2^e, 2^(e+1)) are the
+ * multiples of 2^(e-10) (e >= -14; below 2^-14 the multiples of 2^-24), so x is
+ * rounded to a whole number of that quantum. */
+static double round_to_fp16(double x)
+{
+    if (x == 0.0) return 0.0;
+    int e;
+    frexp(x, &e);              /* x = f * 2^e, f in [0.5, 1): x in [2^(e-1), 2^e) */
+    e -= 1;
+    if (e < -14) e = -14;
+    const double quantum = ldexp(1.0, e - 10);
+    const double r = rint(x / quantum) * quantum;   /* x / quantum is exact */
+    return r > 65504.0 ? INFINITY : r;
+}
+
+/* Quantiser, BitLLM Sec. 2.2, eq. (1): q = clip(round(w / s) + z, qmin, qmax)
+ * with s > 0 and integer z.  The page does not say how s and z are chosen;
+ * the reading here is the min-max affine mapping of each (column n, group g)
+ * with zero kept representable, unsigned codes and round half to even:
+ *   lo = min(0, min w),  hi = max(0, max w)           over the group's G rows
+ *   s  = fp16((hi - lo) / (2^k - 1)),  1 if that is 0,  65504 if it overflows
+ *   z  = clamp(round(-lo / s), 0, 2^k - 1)
+ *   q  = clamp(round(w / s) + z, 0, 2^k - 1)
+ * W is fp16 [K][N] widened to doubles (row-major, the orientation of the
+ * codes); codes are uint8 [K][N]; s and z are [N][K/G] doubles holding fp16
+ * values.  The quotients are taken in fp64: for fp16 operands the fp64
+ * quotient never lands on a rounding tie that the exact quotient is not on. */
+int qmm_oracle_quantize(const double *W, int64_t K, int64_t N, int bits, int64_t G,
+                        uint8_t *codes, double *s, double *z)
+{
+    if (bits < 1 || bits > 8 || K < 0 || N < 0 || !groups_ok(K, G)) return -1;
+    if (K > 0 && N > 0 && (!W || !codes || !s || !z)) return -1;
+    const int64_t ngroups = K / G;
+    const double qmax = (double)((1 << bits) - 1);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ngroups; ++g) {
+            double lo = 0.0, hi = 0.0;
+            for (int64_t i = g * G; i < (g + 1) * G; ++i) {
+                const double w = W[i * N + n];
+                if (w < lo) lo = w;
+                if (w > hi) hi = w;
+            }
+            double sg = round_to_fp16((hi - lo) / qmax);
+            if (sg == 0.0) sg = 1.0;
+            if (isinf(sg)) sg = 65504.0;
+            const double zg = fmin(fmax(rint(-lo / sg), 0.0), qmax);
+            for (int64_t i = g * G; i < (g + 1) * G; ++i) {
+                const double q = fmin(fmax(rint(W[i * N + n] / sg) + zg, 0.0), qmax);
+                codes[i * N + n] = (uint8_t)q;
+            }
+            s[n * ngroups + g] = sg;
+            z[n * ngroups + g] = zg;
+        }
+    }
+    return 0;
 }

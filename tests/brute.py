@@ -110,3 +110,62 @@ def read_page_facts(path: str) -> dict:
             name, *kvs = line.split()
             facts[name] = {k: int(v) for k, v in (kv.split("=") for kv in kvs)}
     return facts
+
+
+def _fp16_positive_table():
+    """Every finite fp16 value >= 0, ascending, as exact Fractions with its bit pattern."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    return [Fraction(float(v)) for v in vals], bits
+
+
+_FP16 = None
+
+
+def nearest_fp16(r: Fraction):
+    """Nearest finite fp16 value to r >= 0 by search over the whole table (ties to
+    the even bit pattern); None past the largest finite value plus half its spacing."""
+    global _FP16
+    if _FP16 is None:
+        _FP16 = _fp16_positive_table()
+    vals, bits = _FP16
+    top = vals[-1]
+    if r >= top + (top - vals[-2]) / 2:
+        return None
+    import bisect
+    j = bisect.bisect_left(vals, r)
+    if j < len(vals) and vals[j] == r:
+        return vals[j]
+    lo, hi = vals[j - 1], vals[j]
+    if r - lo < hi - r:
+        return lo
+    if hi - r < r - lo:
+        return hi
+    return lo if int(bits[j - 1]) % 2 == 0 else hi
+
+
+def exact_quantize(W, bits: int, G: int):
+    """Quantiser of eq. (1) with the min-max (zero-including) reading, in exact rational
+    arithmetic: codes [K][N], s and z [N][K/G] as Fractions."""
+    K, N = W.shape
+    qmax = (1 << bits) - 1
+    ng = K // G
+    codes = np.zeros((K, N), dtype=np.int64)
+    s = [[None] * ng for _ in range(N)]
+    z = [[None] * ng for _ in range(N)]
+    for n in range(N):
+        for g in range(ng):
+            col = [Fraction(float(W[i, n])) for i in range(g * G, (g + 1) * G)]
+            lo = min([Fraction(0)] + col)
+            hi = max([Fraction(0)] + col)
+            sg = nearest_fp16((hi - lo) / qmax)
+            if sg is None:
+                sg = Fraction(65504)
+            elif sg == 0:
+                sg = Fraction(1)
+            zg = min(max(round(-lo / sg), 0), qmax)
+            for r, w in enumerate(col):
+                codes[g * G + r, n] = min(max(round(w / sg) + zg, 0), qmax)
+            s[n][g] = sg
+            z[n][g] = Fraction(zg)
+    return codes, s, z

@@ -289,4 +289,78 @@ def pin_w4a8_rejects_fractional_z(orc):
     raise AssertionError("fractional zero-point accepted")
 
 
+# --------------------------------------------------------------- quantiser ---
+def _quantize_cases():
+    """Tiny fp16 weight matrices with the special groups of the reading: random
+    normals, exact rounding ties, constant (zero, positive, negative) groups,
+    ranges that overflow or underflow the fp16 scale."""
+    rng = np.random.default_rng(1800)
+    K, N, G = 64, 6, 16
+    W = rng.normal(0.0, 0.05, (K, N)).astype(np.float16)
+    W[0:16, 1] = 0                                   # all-zero group
+    W[16:32, 1] = np.float16(0.75)                   # constant positive group
+    W[32:48, 1] = np.float16(-3.0)                   # constant negative group
+    W[0:16, 2] = np.arange(16, dtype=np.float16) * np.float16(0.5)   # w / s on half steps at k = 5
+    W[16:32, 2] = np.float16(-60000.0)               # range past the fp16 scale at k = 1
+    W[17, 2] = np.float16(60000.0)
+    W[32:48, 2] = np.float16(2.0 ** -24)             # a scale that underflows fp16
+    W[48:64, 3] = np.linspace(-1, 1, 16).astype(np.float16)
+    W[48:64, 2] = np.array([0, 3, 0.5, 1.5, 2.5, 0.5, 1.5, 2.5, 1, 2, 0, 3, 2.5, 0.5, 1.5, 3],
+                           dtype=np.float16)      # s = 1 at k = 2: every w / s a tie or a whole number
+    return W, G
+
+
+def pin_quantize_bruteforce(orc):
+    """Codes, s and z bit-exact against exact rational arithmetic and a search
+    over every fp16 value, for every code width."""
+    W, G = _quantize_cases()
+    for bits in range(1, 9):
+        codes, s, z = orc.quantize(W, bits, G)
+        cx, sx, zx = brute.exact_quantize(W, bits, G)
+        assert np.array_equal(codes.astype(np.int64), cx), bits
+        for n in range(W.shape[1]):
+            for g in range(W.shape[0] // G):
+                assert Fraction(float(s[n, g])) == sx[n][g], (bits, n, g)
+                assert Fraction(float(z[n, g])) == zx[n][g], (bits, n, g)
+
+
+def pin_quantize_round_trip(orc):
+    """Weights already on a grid s (q - z), with both code ends present in every
+    group and s a power of two, come back as exactly q, s and z."""
+    rng = np.random.default_rng(1900)
+    for bits in range(1, 9):
+        qmax = (1 << bits) - 1
+        K, N, G = 64, 5, 32
+        q = rng.integers(0, qmax + 1, (K, N))
+        q[0::G, :] = 0
+        q[1::G, :] = qmax
+        z = rng.integers(0, qmax + 1, (N, K // G))
+        sc = 2.0 ** -6
+        W = np.zeros((K, N))
+        for g in range(K // G):
+            W[g * G:(g + 1) * G] = sc * (q[g * G:(g + 1) * G] - z[:, g][None, :])
+        W16 = W.astype(np.float16)
+        assert np.array_equal(W16.astype(np.float64), W)
+        codes, s, zz = orc.quantize(W16, bits, G)
+        assert np.array_equal(codes.astype(np.int64), q), bits
+        assert np.all(s.astype(np.float64) == sc) and np.array_equal(zz.astype(np.int64), z), bits
+
+
+def pin_quantize_error_bound(orc):
+    """Every weight is reproduced within one step s (half a step from rounding,
+    at most half more from the fp16 rounding of s at the clipped ends), and zero
+    exactly."""
+    rng = np.random.default_rng(2000)
+    K, N, G = 256, 7, 64
+    W = rng.normal(0.0, 0.02, (K, N)).astype(np.float16)
+    W[5, :] = 0
+    for bits in range(1, 9):
+        codes, s, z = orc.quantize(W, bits, G)
+        s64 = np.repeat(s.astype(np.float64).T, G, axis=0)
+        z64 = np.repeat(z.astype(np.float64).T, G, axis=0)
+        deq = (codes.astype(np.float64) - z64) * s64
+        assert np.all(np.abs(deq - W.astype(np.float64)) <= s64 * 1.0), bits
+        assert np.all(deq[5, :] == 0), bits
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

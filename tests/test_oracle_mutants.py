@@ -51,6 +51,18 @@ MUTANTS = {
     "w4a8_token_scale_dropped": ("Y[m * N + n] = sx[m] * y;", "Y[m * N + n] = y;"),
     "w4a8_group_short": ("for (int64_t i = g * G; i < (g + 1) * G; ++i)",
                          "for (int64_t i = g * G; i + 1 < (g + 1) * G; ++i)"),
+    "quantize_range_without_zero": ("            double lo = 0.0, hi = 0.0;\n",
+                                    "            double lo = W[g * G * N + n], hi = W[g * G * N + n];\n"),
+    "quantize_round_half_up": ("const double q = fmin(fmax(rint(W[i * N + n] / sg) + zg, 0.0), qmax);",
+                               "const double q = fmin(fmax(floor(W[i * N + n] / sg + 0.5) + zg, 0.0), qmax);"),
+    "quantize_zero_point_sign": ("const double zg = fmin(fmax(rint(-lo / sg), 0.0), qmax);",
+                                 "const double zg = fmin(fmax(rint(lo / sg), 0.0), qmax);"),
+    "quantize_levels_off_by_one": ("const double qmax = (double)((1 << bits) - 1);",
+                                   "const double qmax = (double)(1 << bits);"),
+    "quantize_scale_truncated": ("const double r = rint(x / quantum) * quantum;",
+                                 "const double r = floor(x / quantum) * quantum;"),
+    "quantize_scale_not_fp16": ("double sg = round_to_fp16((hi - lo) / qmax);",
+                                "double sg = (hi - lo) / qmax;"),
     "sampled_drops_scale": ("            double w = (q - zero_point(z, n, g, ngroups, bits)) * s[n * ngroups + g];",
                             "            double w = (q - zero_point(z, n, g, ngroups, bits));"),
 }
