@@ -18,8 +18,9 @@ kernel's algorithmic bytes (packed weights + scales + x + y) per launch
 against that mean launch duration and the 8 TB/s HBM peak.  The same JSON line carries the M = 2048
 prefill product (qmm_gemm) in TFLOP/s against the 2.5 PFLOP/s dense fp16 MFMA
 peak, the batched-decode (70B MLP-up shapes, M = 1, 8, 16, k = 1, 2, 5, 7, 8) and
-W4A8 / W8A8 (8B MLP shapes, M = 16, 4- and 8-bit weights) products as a
-"suite" object, and the CPU oracle timed on this host on a bounded sample.
+W4A8 / W8A8 (8B MLP shapes, M = 16, 4- and 8-bit weights) products and the
+quantiser (7B MLP weight) as a "suite" object, and the CPU oracle timed on
+this host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-suite]
 """
@@ -246,6 +247,33 @@ def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
 
 
+def quantize_suite(torch, q, synthetic, timer, reps):
+    """qmm_quantize on the 7B MLP weight (K 4096, N 11008, G 128, k 4): fp16 W in,
+    codes, s and z out; HBM-bound."""
+    w = synthetic.DECODE_7B
+    K, N, G, bits = w["K"], w["N"], w["G"], 4
+    g = synthetic.rng(synthetic.seed_for(2, bits, 9))
+    W = (torch.from_numpy(synthetic.fp16_normal(g, (K, N))).to("cuda:0") * 0.02).to(torch.float16)
+    per = K * N * 2
+    Ws = [W] + [W.clone() for _ in range(max(1, -(-(1 << 30) // per)) - 1)]
+    codes = torch.empty((K, N), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((N, K // G), dtype=torch.float16, device="cuda:0")
+    z = torch.empty_like(s)
+    state = {"i": 0}
+
+    def launch(i):
+        state["i"] += 1
+        q.quantize(Ws[state["i"] % len(Ws)], bits, G, codes=codes, s=s, z=z)
+
+    for i in range(3):
+        launch(i)
+    ms = timer.region_ms(launch, reps) / reps
+    alg = K * N * 2 + K * N + N * (K // G) * 4
+    return {"workload": f"quantize 7B-MLP K{K} N{N} k{bits} G{G}", "us": round(ms * 1e3, 2),
+            "algorithmic_GBs": round(alg / ms / 1e6, 1),
+            "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,7 +358,8 @@ def main():
         reps = max(10, args.steps // 2)
         suite = {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
                  "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
-                 "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8)}
+                 "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
+                 "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps)}
 
     cpu = None
     if not args.no_cpu:

@@ -18,11 +18,11 @@ import torch
 
 from ._build import LIBRARY
 
-__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "library_path",
-           "SYMBOLS"]
+__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "quantize",
+           "library_path", "SYMBOLS"]
 
 SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8",
-           "qmm_status_string", "qmm_last_error")
+           "qmm_quantize", "qmm_status_string", "qmm_last_error")
 
 
 class QmmError(RuntimeError):
@@ -44,6 +44,7 @@ def _load():
         "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm_w4a8": ([P, P, P, P, P, P, P, I64, I64, I64, I64, P], INT),
         "qmm_gemm_wka8": ([P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_quantize": ([P, P, P, P, I64, I64, INT, I64, P], INT),
         "qmm_status_string": ([INT], ctypes.c_char_p),
         "qmm_last_error": ([], ctypes.c_char_p),
     }
@@ -168,3 +169,20 @@ def _int8_product(any_bits: bool, Xq, sx, wq, s, z, bits: int, G: int, out, acc_
     else:
         _check(_lib.qmm_gemm_w4a8(*ptrs, M, K, N, G, _stream(Xq.device)))
     return out
+
+
+def quantize(W, bits: int, G: int, codes=None, s=None, z=None):
+    """(codes uint8 [K, N], s fp16 [N, K/G], z fp16 [N, K/G]) for fp16 weights W [K, N]."""
+    _need(W, "W", torch.float16)
+    K, N = W.shape
+    if codes is None:
+        codes = torch.empty((K, N), dtype=torch.uint8, device=W.device)
+    if s is None:
+        s = torch.empty((N, K // G), dtype=torch.float16, device=W.device)
+    if z is None:
+        z = torch.empty((N, K // G), dtype=torch.float16, device=W.device)
+    _need(codes, "codes", torch.uint8, (K, N), W.device)
+    _need(s, "s", torch.float16, (N, K // G), W.device)
+    _need(z, "z", torch.float16, (N, K // G), W.device)
+    _check(_lib.qmm_quantize(_ptr(W), _ptr(codes), _ptr(s), _ptr(z), K, N, bits, G, _stream(W.device)))
+    return codes, s, z

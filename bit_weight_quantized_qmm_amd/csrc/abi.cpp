@@ -134,6 +134,17 @@ qmm_status qmm_gemm_wka8(const int8_t *Xq, const qmm_half *sx, const uint32_t *w
     return int8_product("qmm_gemm_wka8", Xq, sx, wq, s, z, Y, acc_out, M, K, N, bits, G, stream);
 }
 
+qmm_status qmm_quantize(const qmm_half *W, uint8_t *codes, qmm_half *s, qmm_half *z, int64_t K, int64_t N, int bits,
+                        int64_t G, qmm_stream stream)
+{
+    const char *fn = "qmm_quantize";
+    qmm_status st = check_shape(fn, 1, K, N, bits, G, true);
+    if (st != QMM_OK) return st;
+    if (!W || !codes || !s || !z) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (K / G > 65535) return fail(QMM_ERR_UNSUPPORTED, "%s: more than 65535 groups per column", fn);
+    return hip_status(qmm::launch_quantize(W, codes, s, z, (int)K, (int)N, bits, (int)G, (hipStream_t)stream), fn);
+}
+
 const char *qmm_status_string(qmm_status status)
 {
     switch (status) {

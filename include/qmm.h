@@ -139,6 +139,26 @@ qmm_status qmm_gemm_wka8(const int8_t *Xq, const qmm_half *sx, const uint32_t *w
                          const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M, int64_t K,
                          int64_t N, int bits, int64_t G, qmm_stream stream);
 
+/* Quantiser: fp16 weights -> k-bit codes and one fp16 (s, z) per (column,
+ * group), after BitLLM Sec. 2.2, eq. (1): q = clip(round(w / s) + z, 0, 2^k - 1)
+ * with s > 0 and integer z.  The page leaves the choice of s and z open; here
+ * it is the min-max affine mapping of each group with zero kept representable:
+ *   lo = min(0, min w),  hi = max(0, max w)       over the group's G rows
+ *   s  = fp16((hi - lo) / (2^k - 1))  (rounded once, ties to even; 1 if that
+ *        is 0, 65504 if it overflows)
+ *   z  = clamp(round(-lo / s), 0, 2^k - 1),  q = clamp(round(w / s) + z, 0, 2^k - 1)
+ * with round half to even and the quotients exact in their rounding decisions.
+ * The result is what qmm_pack, qmm_gemv and qmm_gemm take: codes uint8 [K][N]
+ * (row-major, the orientation of W), s and z fp16 [N][K/G].
+ *   W      device, fp16 [K][N] row-major, finite values
+ *   codes  device, uint8 [K][N] (written)
+ *   s, z   device, fp16 [N][K/G] (written; z holds integers)
+ * K, N, bits and G as for qmm_gemv (K % 32 == 0, G % 32 == 0, K % G == 0,
+ * bits 1..8); K / G > 65535 gives QMM_ERR_UNSUPPORTED.  No allocation, no
+ * synchronisation; enqueued on stream. */
+qmm_status qmm_quantize(const qmm_half *W, uint8_t *codes, qmm_half *s, qmm_half *z, int64_t K, int64_t N,
+                        int bits, int64_t G, qmm_stream stream);
+
 /* Static text for a status code. */
 const char *qmm_status_string(qmm_status status);
 

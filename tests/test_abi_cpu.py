@@ -38,6 +38,8 @@ def lib():
     lib.qmm_gemm_w4a8.restype = INT
     lib.qmm_gemm_wka8.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P]
     lib.qmm_gemm_wka8.restype = INT
+    lib.qmm_quantize.argtypes = [P, P, P, P, I64, I64, INT, I64, P]
+    lib.qmm_quantize.restype = INT
     lib.qmm_status_string.argtypes = [INT]
     lib.qmm_status_string.restype = ctypes.c_char_p
     lib.qmm_last_error.restype = ctypes.c_char_p
@@ -46,7 +48,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
-    for name in ("qmm_pack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8"):
+    for name in ("qmm_pack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8", "qmm_quantize"):
         assert name in syms
 
 
@@ -131,6 +133,20 @@ def test_wka8_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 8, 64, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 3, 2048, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4000, 64, 8, 128, None) == INVALID
+
+
+def test_quantize_validation(lib):
+    """Host-side checks only (every call returns before any HIP call)."""
+    f = lib.qmm_quantize
+    assert f(None, FAKE, FAKE, FAKE, 256, 8, 4, 64, None) == INVALID
+    assert f(FAKE, None, FAKE, FAKE, 256, 8, 4, 64, None) == INVALID
+    assert f(FAKE, FAKE, None, FAKE, 256, 8, 4, 64, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, None, 256, 8, 4, 64, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 8, 9, 64, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 8, 4, 48, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 250, 8, 4, 50, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 0, 4, 64, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 32 * 65536, 1, 4, 32, None) == UNSUPPORTED
 
 
 def test_status_strings(lib):

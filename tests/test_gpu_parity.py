@@ -396,3 +396,61 @@ def test_w8a8_workload(q, orc):
     check_wka8(orc, c, 8, Y, acc)
     Y2, _ = run_wka8(q, c, 8, with_acc=False)
     assert torch.equal(Y.cpu(), Y2.cpu())
+
+
+# ------------------------------------------------------------- quantiser ---
+def check_quantize(q, orc, W, bits, G):
+    codes, s, z = q.quantize(dev(W), bits, G)
+    cx, sx, zx = orc.quantize(W, bits, G)
+    assert np.array_equal(codes.cpu().numpy(), cx)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), sx.view(np.uint16))
+    assert np.array_equal(z.cpu().numpy().view(np.uint16), zx.view(np.uint16))
+    return codes, s, z
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("K,N,G", [(256, 300, 64), (1024, 70, 128), (96, 513, 32)])
+def test_quantize_small(q, orc, bits, K, N, G):
+    """Codes, s and z bit-exact on LLM-like weights: several column blocks and
+    a ragged column tail."""
+    rng = np.random.default_rng(synthetic.seed_for(99, bits, K + N))
+    W = rng.normal(0.0, 0.02, (K, N)).astype(np.float16)
+    W[:, ::7] *= np.float16(8.0)                   # a few wide columns
+    check_quantize(q, orc, W, bits, G)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4, 8])
+def test_quantize_special_groups(q, orc, bits):
+    """Constant groups (zero, positive, negative), a range past the fp16 scale, a
+    scale that underflows, exact rounding ties, and the largest fp16 values."""
+    K, N, G = 128, 260, 32
+    rng = np.random.default_rng(41 + bits)
+    W = rng.normal(0.0, 0.05, (K, N)).astype(np.float16)
+    W[0:32, 1] = 0
+    W[32:64, 1] = np.float16(0.75)
+    W[64:96, 1] = np.float16(-3.0)
+    W[0:32, 2] = np.float16(-60000.0)
+    W[1, 2] = np.float16(60000.0)
+    W[32:64, 2] = np.float16(2.0 ** -24)
+    W[64:96, 2] = np.tile(np.array([0, 3, 0.5, 1.5, 2.5, 0.5, 1.5, 2.5, 1, 2, 0, 3, 2.5, 0.5, 1.5, 3],
+                                   dtype=np.float16), 2)
+    W[0:32, 3] = np.float16(65504.0)
+    W[0:32, 4] = np.float16(-65504.0)
+    W[:, 259] = np.arange(K, dtype=np.float16) * np.float16(0.25)
+    check_quantize(q, orc, W, bits, G)
+
+
+def test_quantize_feeds_the_product(q, orc):
+    """quantize -> pack -> qmm_gemv on the 7B decode shape: codes, s, z bit-exact,
+    and the product of the quantised weights within tolerance of the oracle."""
+    w = synthetic.DECODE_7B
+    K, N, G = w["K"], w["N"], w["G"]
+    rng = np.random.default_rng(synthetic.seed_for(2, 4, 77))
+    W = rng.normal(0.0, 0.02, (K, N)).astype(np.float16)
+    codes, s, z = check_quantize(q, orc, W, 4, G)
+    X = synthetic.fp16_normal(synthetic.rng(5), (1, K))
+    wq = q.pack(codes, 4)
+    Y = q.gemv(dev(X), wq, s, z, 4, G)
+    cx, sx, zx = orc.quantize(W, 4, G)
+    ref = orc.qmm(X, orc.pack(cx, 4), sx, zx, 4, G)
+    assert rel_err(Y, ref) <= TOL
