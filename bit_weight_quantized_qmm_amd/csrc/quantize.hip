@@ -7,13 +7,15 @@
 //   lo = min(0, min w),  hi = max(0, max w)
 //   s  = fp16((hi - lo) / (2^k - 1)),  1 if that is 0,  65504 if it overflows
 //   z  = clamp(round(-lo / s), 0, 2^k - 1),  q = clamp(round(w / s) + z, 0, 2^k - 1)
-// The quotients are fp64, so each rounding decision is the one the exact
-// quotient gives (fp16 operands never produce a false tie in fp64).  The codes
-// feed qmm_pack.
+// Every rounding decision is the one the exact quotient gives
+// (round_quotient).  The codes feed qmm_pack.
 //
-// One thread per (column, group): the G rows of a column are read down the
-// row-major matrix, consecutive threads on consecutive columns, twice (range,
-// then codes; the second pass hits the cache).
+// A wave covers 16 column slots of VEC adjacent columns (8-byte loads when
+// VEC = 4: 128 contiguous bytes of a row per 16 lanes) and splits a group's G
+// rows into 4 parts, one per 16-lane row of the wave; the part ranges are
+// combined with two lane shuffles.  Each lane reads its rows twice: range, then
+// codes (the second pass hits the cache; keeping the rows in registers instead
+// measured slower).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -34,41 +36,118 @@ __device__ __forceinline__ _Float16 fp16_of_double(double x)
     return (_Float16)f;
 }
 
-template <int BITS>
+// round(w / s), ties to even, for fp16 values w and s > 0 (inv = fp32 1 / s,
+// half = s / 2).  t0 = rint(w * inv) is within one of the answer while
+// |w / s| < 2^21 (beyond, the clamp to the code range decides).  The residual
+// w - t0 s from one fma is exact at a tie (it is then s / 2, representable)
+// and otherwise at least about 2^-23 s away from s / 2 (w and (t0 + 1/2) s are
+// multiples of a common power of two), more than the fma's rounding, so its
+// comparisons with s / 2 decide exactly.
+__device__ __forceinline__ float round_quotient(float w, float s, float inv, float half)
+{
+    float t = __builtin_rintf(w * inv);
+    const float r = __builtin_fmaf(-t, s, w);
+    const bool odd = ((int)t & 1) != 0;   // |t| < 2^21 wherever a tie can change the code
+    if (r > half || (r == half && odd)) t += 1.0f;
+    else if (r < -half || (r == -half && odd)) t -= 1.0f;
+    return t;
+}
+
+template <int BITS, int VEC>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ W, uint8_t *__restrict__ codes,
                                                        uint16_t *__restrict__ s, uint16_t *__restrict__ z, int K, int N,
                                                        int G)
 {
-    const int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;   // no barrier in this kernel
-    const int g = blockIdx.y, ng = K / G;
-    constexpr double QMAX = (double)((1 << BITS) - 1);
-    const size_t base = (size_t)g * G * N + n;
+    const int lane = threadIdx.x & 63, c = lane & 15, part = lane >> 4;
+    const int n0 = ((blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * 16 + c) * VEC;
+    const bool live = n0 < N;   // every lane stays for the shuffles
+    const int g = blockIdx.y, ng = K / G, rows = G >> 2;
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    const size_t base = ((size_t)g * G + (size_t)part * rows) * N + n0;
 
-    float lo = 0.f, hi = 0.f;
-    for (int r = 0; r < G; ++r) {
-        const float w = (float)as_half(W[base + (size_t)r * N]);
-        lo = fminf(lo, w);
-        hi = fmaxf(hi, w);
+    auto load = [&](int r, float (&w)[VEC]) {
+        const size_t at = base + (size_t)r * N;
+        if constexpr (VEC == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(W + at);
+            const half2_t a = as_half2(v.x), b = as_half2(v.y);
+            w[0] = (float)a[0];
+            w[1] = (float)a[1];
+            w[2] = (float)b[0];
+            w[3] = (float)b[1];
+        } else {
+            w[0] = (float)as_half(W[at]);
+        }
+    };
+
+    float lo[VEC], hi[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) lo[v] = hi[v] = 0.f;
+    if (live) {
+#pragma unroll 8
+        for (int r = 0; r < rows; ++r) {
+            float w[VEC];
+            load(r, w);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                lo[v] = fminf(lo[v], w[v]);
+                hi[v] = fmaxf(hi[v], w[v]);
+            }
+        }
     }
-    _Float16 sh = fp16_of_double(((double)hi - (double)lo) / QMAX);
-    if (sh == (_Float16)0.0f) sh = (_Float16)1.0f;
-    if (__builtin_isinf((float)sh)) sh = (_Float16)65504.0f;
-    const double sg = (double)sh;
-    const double zg = fmin(fmax(__builtin_rint(-(double)lo / sg), 0.0), QMAX);
-    for (int r = 0; r < G; ++r) {
-        const double w = (double)as_half(W[base + (size_t)r * N]);
-        codes[base + (size_t)r * N] = (uint8_t)fmin(fmax(__builtin_rint(w / sg) + zg, 0.0), QMAX);
+    float sg[VEC], inv[VEC], half[VEC], zg[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        // the four row parts of a column sit 16 lanes apart
+        lo[v] = fminf(lo[v], __shfl_xor(lo[v], 16));
+        lo[v] = fminf(lo[v], __shfl_xor(lo[v], 32));
+        hi[v] = fmaxf(hi[v], __shfl_xor(hi[v], 16));
+        hi[v] = fmaxf(hi[v], __shfl_xor(hi[v], 32));
+        _Float16 sh = fp16_of_double(((double)hi[v] - (double)lo[v]) / (double)QMAX);
+        if (sh == (_Float16)0.0f) sh = (_Float16)1.0f;
+        if (__builtin_isinf((float)sh)) sh = (_Float16)65504.0f;
+        sg[v] = (float)sh;
+        inv[v] = 1.0f / sg[v];
+        half[v] = 0.5f * sg[v];
+        zg[v] = fminf(fmaxf(round_quotient(-lo[v], sg[v], inv[v], half[v]), 0.f), QMAX);
+        if (part == 0 && n0 + v < N) {
+            s[(size_t)(n0 + v) * ng + g] = as_u16(sh);
+            z[(size_t)(n0 + v) * ng + g] = as_u16((_Float16)zg[v]);
+        }
     }
-    s[(size_t)n * ng + g] = as_u16(sh);
-    z[(size_t)n * ng + g] = as_u16((_Float16)zg);
+    if (!live) return;
+#pragma unroll 8
+    for (int r = 0; r < rows; ++r) {
+        float w[VEC];
+        load(r, w);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float q = fminf(fmaxf(round_quotient(w[v], sg[v], inv[v], half[v]) + zg[v], 0.f), QMAX);
+            packed |= (uint32_t)q << (8 * v);
+        }
+        const size_t at = base + (size_t)r * N;
+        if constexpr (VEC == 4)
+            *reinterpret_cast<uint32_t *>(codes + at) = packed;
+        else
+            codes[at] = (uint8_t)packed;
+    }
 }
 
 hipError_t launch_quantize(const uint16_t *W, uint8_t *codes, uint16_t *s, uint16_t *z, int K, int N, int bits, int G,
                            hipStream_t st)
 {
-    const dim3 block(256), grid((unsigned)((N + 255) / 256), (unsigned)(K / G));
-#define QMM_Q(B) hipLaunchKernelGGL(quantize_kernel<B>, grid, block, 0, st, W, codes, s, z, K, N, G)
+    // four columns per thread when every row of W and of the codes stays 8- and
+    // 4-byte aligned
+    const bool vec = N % 4 == 0 && reinterpret_cast<uintptr_t>(W) % 8 == 0 && reinterpret_cast<uintptr_t>(codes) % 4 == 0;
+    const int per_block = vec ? 256 : 64;   // 4 waves of 16 column slots
+    const dim3 block(256), grid((unsigned)((N + per_block - 1) / per_block), (unsigned)(K / G));
+#define QMM_Q(B)                                                                                                \
+    do {                                                                                                        \
+        if (vec)                                                                                                \
+            hipLaunchKernelGGL((quantize_kernel<B, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);           \
+        else                                                                                                    \
+            hipLaunchKernelGGL((quantize_kernel<B, 1>), grid, block, 0, st, W, codes, s, z, K, N, G);           \
+    } while (0)
     switch (bits) {
         case 1: QMM_Q(1); break;
         case 2: QMM_Q(2); break;
