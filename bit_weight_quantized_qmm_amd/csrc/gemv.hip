@@ -871,7 +871,9 @@ static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
 }
 
 // M = 1 with K <= 16384 and at most 64 columns per wave: RPL = runs per lane
-// (1, 2, 4, 8), D = 8 / RPL columns in flight per wave.
+// (1, 2, 4, 8), D = 8 / RPL columns in flight per wave; 4 for RPL = 4 and
+// k <= 2, whose columns carry few bytes (k = 2 on the 70B MLP-up shape: 19.4
+// -> 17.2 us; 8 in flight, or two workgroups per CU, measured slower).
 template <int BITS, bool PGZ>
 static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
 {
@@ -879,7 +881,7 @@ static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
     const int rpl_need = (R + 63) / 64;
     if (rpl_need <= 1) return gemv_m1_go<BITS, 1, 8, 1, PGZ>(a, st);
     if (rpl_need <= 2) return gemv_m1_go<BITS, 2, 4, 1, PGZ>(a, st);
-    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, 2, 1, PGZ>(a, st);
+    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, (BITS <= 2 ? 4 : 2), 1, PGZ>(a, st);
     return gemv_m1_go<BITS, 8, 1, 2, PGZ>(a, st);
 }
 
