@@ -61,6 +61,7 @@ KERNEL_SOURCES = {
     "gemv_m1": ("gemv.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
     "gemm": ("gemm.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
     "w4a8": ("w4a8.hip", "qmm_device.hpp", "launch.hpp"),
+    "quantize": ("quantize.hip", "qmm_device.hpp", "launch.hpp"),
 }
 
 

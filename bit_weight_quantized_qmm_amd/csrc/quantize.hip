@@ -14,8 +14,9 @@
 // VEC = 4: 128 contiguous bytes of a row per 16 lanes) and splits a group's G
 // rows into 4 parts, one per 16-lane row of the wave; the part ranges are
 // combined with two lane shuffles.  Each lane reads its rows twice: range, then
-// codes (the second pass hits the cache; keeping the rows in registers instead
-// measured slower).
+// codes.  The resident waves' rows exceed L2, so the second pass fetches W
+// again from beyond it (keeping the rows in registers instead measured
+// slower).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
