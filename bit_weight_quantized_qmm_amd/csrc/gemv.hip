@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
         const uint32_t n = (uint32_t)(w + i * W);
 #pragma unroll
         for (int j = 0; j < RPL; ++j) {
-            load_dwords<LOAD_STREAM>(wr, n * col_bytes + roff[j], d[slot][j], BITS);
+            // default cache policy: the non-temporal hint measured slower here
+            // (7B decode k = 6: 9.1 -> 8.0 us; 70B M = 1 k = 5: 31.8 -> 27.1 us)
+            load_dwords<LOAD_DEFAULT>(wr, n * col_bytes + roff[j], d[slot][j], BITS);
             const uint32_t so = (n * (uint32_t)ng + (uint32_t)gi[j]) * 2u;
             sv[slot][j] = __builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
             zv[slot][j] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, so, 0, 0) : (uint16_t)0;
@@ -642,7 +644,10 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     auto issue = [&](int j, int st, int slot) {
         const int t = wave * S + st;
         const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
-        load_dwords<LOAD_STREAM>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * run_bytes : OOB, d[slot], BITS);
+        // default cache policy: a unit's runs cut cache lines that the wave's next
+        // unit reads, and with the non-temporal hint those lines were fetched
+        // again (70B MLP-up M = 8, k = 5: 68 -> 42 us)
+        load_dwords<LOAD_DEFAULT>(wr, j < ntile ? col * col_bytes + (uint32_t)(4 * t + g) * run_bytes : OOB, d[slot], BITS);
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(u / S, u % S, u);
