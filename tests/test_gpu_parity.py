@@ -454,3 +454,25 @@ def test_quantize_feeds_the_product(q, orc):
     cx, sx, zx = orc.quantize(W, 4, G)
     ref = orc.qmm(X, orc.pack(cx, 4), sx, zx, 4, G)
     assert rel_err(Y, ref) <= TOL
+
+
+# ------------------------------------- more column tiles than one round ---
+@pytest.mark.parametrize("bits,M,pgz", [(3, 8, True), (8, 2, False), (5, 16, True)])
+def test_gemv_many_tiles(q, orc, bits, M, pgz):
+    """More 16-column tiles than 8 per CU: the M >= 2 kernel's workgroups run in
+    several rounds, the last one ragged (N not a multiple of 16)."""
+    K, N, G = 1024, 40003, 128
+    c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(93, bits, M), per_group_z=pgz)
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 8, 3])
+def test_wka8_many_tiles(q, orc, bits):
+    """The int8-activation streaming kernel past one round of workgroups, two M
+    tiles, a ragged column tail; int32 group sums bit-exact."""
+    M, K, N, G = 20, 1024, 40003, 256
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(94, bits), bits=bits, per_group_z=True)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
