@@ -18,10 +18,10 @@ import torch
 
 from ._build import LIBRARY
 
-__all__ = ["QmmError", "packed_bytes", "pack", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "quantize",
+__all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "quantize",
            "library_path", "SYMBOLS"]
 
-SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8",
+SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8",
            "qmm_quantize", "qmm_status_string", "qmm_last_error")
 
 
@@ -39,6 +39,7 @@ def _load():
     sig = {
         "qmm_packed_bytes": ([I64, I64, INT], ctypes.c_size_t),
         "qmm_pack": ([P, P, I64, I64, INT, P], INT),
+        "qmm_pack_signed": ([P, P, I64, I64, INT, P], INT),
         "qmm_unpack": ([P, P, I64, I64, INT, P], INT),
         "qmm_gemv": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
@@ -100,6 +101,17 @@ def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> tor
         out = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
     _need(out, "out", torch.int32, (N, K * bits // 32), codes.device)
     _check(_lib.qmm_pack(_ptr(codes), _ptr(out), K, N, bits, _stream(codes.device)))
+    return out
+
+
+def pack_signed(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 two's-complement codes [K, N] -> packed stream (offset-binary: q + 2^(bits-1))."""
+    _need(codes, "codes", torch.int8)
+    K, N = codes.shape
+    if out is None:
+        out = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
+    _need(out, "out", torch.int32, (N, K * bits // 32), codes.device)
+    _check(_lib.qmm_pack_signed(_ptr(codes), _ptr(out), K, N, bits, _stream(codes.device)))
     return out
 
 

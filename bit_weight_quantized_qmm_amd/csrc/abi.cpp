@@ -68,7 +68,18 @@ qmm_status qmm_pack(const uint8_t *codes, uint32_t *wq, int64_t K, int64_t N, in
     qmm_status st = check_shape("qmm_pack", 1, K, N, bits, 32, false);
     if (st != QMM_OK) return st;
     if (!codes || !wq) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", "qmm_pack");
-    return hip_status(qmm::launch_pack(codes, wq, (int)K, (int)N, bits, (hipStream_t)stream), "qmm_pack");
+    return hip_status(qmm::launch_pack(codes, wq, (int)K, (int)N, bits, false, (hipStream_t)stream), "qmm_pack");
+}
+
+qmm_status qmm_pack_signed(const int8_t *codes, uint32_t *wq, int64_t K, int64_t N, int bits, qmm_stream stream)
+{
+    const char *fn = "qmm_pack_signed";
+    qmm_status st = check_shape(fn, 1, K, N, bits, 32, false);
+    if (st != QMM_OK) return st;
+    if (!codes || !wq) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    return hip_status(qmm::launch_pack(reinterpret_cast<const uint8_t *>(codes), wq, (int)K, (int)N, bits, true,
+                                       (hipStream_t)stream),
+                      fn);
 }
 
 qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, int bits, qmm_stream stream)

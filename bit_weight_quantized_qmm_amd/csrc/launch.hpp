@@ -26,7 +26,7 @@ struct W4A8Args {
     int M, K, N, bits, G;
 };
 
-hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, hipStream_t st);
+hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, bool is_signed, hipStream_t st);
 hipError_t launch_unpack(const uint32_t *wq, uint8_t *codes, int K, int N, int bits, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st);

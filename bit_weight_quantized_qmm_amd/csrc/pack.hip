@@ -2,7 +2,8 @@
 //
 // One thread owns one (column n, run r) pair: 32 codes = k dwords.  Threads of
 // a wave take consecutive columns, so the strided code reads codes[(32r+i)*N+n]
-// are coalesced across the wave.
+// are coalesced across the wave.  Signed (two's complement) codes are stored
+// offset-binary, q + 2^(k-1): the low k bits with the top one flipped (flip).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -10,7 +11,7 @@ namespace qmm {
 
 template <int BITS>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ codes, uint32_t *__restrict__ wq,
-                                                   int K, int N)
+                                                   int K, int N, uint32_t flip)
 {
     const int R = K >> 5;
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     const uint8_t *src = codes + (size_t)(32 * r) * N + n;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const uint32_t q = src[(size_t)i * N] & ((1u << BITS) - 1u);
+        const uint32_t q = (src[(size_t)i * N] ^ flip) & ((1u << BITS) - 1u);
         const int b = i * BITS, j = b >> 5, sh = b & 31;
         d[j] |= q << sh;
         if (sh + BITS > 32) d[j + 1] |= q >> (32 - sh);
@@ -59,12 +60,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t *__restrict_
     }
 }
 
-hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, hipStream_t st)
+hipError_t launch_pack(const uint8_t *codes, uint32_t *wq, int K, int N, int bits, bool is_signed, hipStream_t st)
 {
     const long long total = (long long)(K / 32) * N;
     const dim3 block(256), grid((unsigned)((total + 255) / 256));
+    const uint32_t flip = is_signed ? 1u << (bits - 1) : 0u;
     switch (bits) {
-#define QMM_CASE(B) case B: hipLaunchKernelGGL(pack_kernel<B>, grid, block, 0, st, codes, wq, K, N); break;
+#define QMM_CASE(B) case B: hipLaunchKernelGGL(pack_kernel<B>, grid, block, 0, st, codes, wq, K, N, flip); break;
         QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
         default: return hipErrorInvalidValue;

@@ -78,6 +78,18 @@ size_t qmm_packed_bytes(int64_t K, int64_t N, int bits);
 qmm_status qmm_pack(const uint8_t *codes, uint32_t *wq, int64_t K, int64_t N, int bits,
                     qmm_stream stream);
 
+/* Pack signed (two's complement) codes [K][N], q in [-2^(bits-1), 2^(bits-1) - 1]
+ * (the low `bits` bits of each int8 are used), into the same stream format,
+ * stored offset-binary: q + 2^(bits-1), i.e. the low bits with the top one
+ * flipped.  Every product entry point then computes with signed codes
+ * unchanged: w = (q_stored - z) s with z = NULL (2^(bits-1)) is q s, and a
+ * signed zero-point z_s is passed as z_s + 2^(bits-1).  The Tilus verdict page
+ * (pith extraction, forward implications) lists int2..int8 beside the unsigned
+ * and float widths one kernel template should cover; here they share the
+ * unsigned kernels outright.  Same arguments, layouts and errors as qmm_pack. */
+qmm_status qmm_pack_signed(const int8_t *codes, uint32_t *wq, int64_t K, int64_t N, int bits,
+                           qmm_stream stream);
+
 /* Test hook: decode Wq back to codes [K][N] with the same in-register unpack
  * (dword runs -> fp16 bit patterns) that qmm_gemv and qmm_gemm use, then read
  * each code back out of its fp16 pattern.  Exact inverse of qmm_pack. */

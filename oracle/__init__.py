@@ -96,6 +96,12 @@ class Oracle:
         self._check(self.lib.qmm_oracle_pack(_ptr(codes), _ptr(out), K, N, bits), "pack")
         return out
 
+    def pack_signed(self, codes, bits: int) -> np.ndarray:
+        """Stream of two's-complement codes [K][N]: stored offset-binary, q + 2^(bits-1)
+        (the reading of signed codes this library takes), then packed as unsigned."""
+        q = (np.asarray(codes, dtype=np.int64) + (1 << (bits - 1))) & ((1 << bits) - 1)
+        return self.pack(q.astype(np.uint8), bits)
+
     def unpack(self, stream, K: int, N: int, bits: int) -> np.ndarray:
         """stream [N][K*bits/8] -> uint8 codes [K][N]."""
         b = self._stream(stream, K, N, bits)

@@ -289,6 +289,27 @@ def pin_w4a8_rejects_fractional_z(orc):
     raise AssertionError("fractional zero-point accepted")
 
 
+# ------------------------------------------------------------ signed codes ---
+def pin_signed_codes_dequantise_to_q_times_s(orc):
+    """Two's-complement codes stored offset-binary: with the default zero-point the
+    dequantised weight is q s exactly, and a signed zero-point z_s passed as
+    z_s + 2^(k-1) gives (q - z_s) s (numpy closed forms)."""
+    rng = np.random.default_rng(2100)
+    for bits in range(1, 9):
+        K, N, G = 64, 5, 32
+        lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+        q = rng.integers(lo, hi + 1, (K, N))
+        q[0, :], q[1, :] = lo, hi
+        s = rng.uniform(0.01, 0.1, (N, K // G)).astype(np.float16)
+        st = orc.pack_signed(q.astype(np.int8), bits)
+        s_rows = np.repeat(s.astype(np.float64).T, G, axis=0)
+        assert np.array_equal(orc.dequant(st, s, None, K, N, bits, G), q * s_rows), bits
+        zs = rng.integers(lo, hi + 1, (N, K // G))
+        z_rows = np.repeat(zs.T, G, axis=0)
+        got = orc.dequant(st, s, (zs + (1 << (bits - 1))).astype(np.float16), K, N, bits, G)
+        assert np.array_equal(got, (q - z_rows) * s_rows), bits
+
+
 # --------------------------------------------------------------- quantiser ---
 def _quantize_cases():
     """Tiny fp16 weight matrices with the special groups of the reading: random

@@ -28,7 +28,7 @@ def lib():
     P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.qmm_packed_bytes.argtypes = [I64, I64, INT]
     lib.qmm_packed_bytes.restype = ctypes.c_size_t
-    for f in ("qmm_pack", "qmm_unpack"):
+    for f in ("qmm_pack", "qmm_pack_signed", "qmm_unpack"):
         getattr(lib, f).argtypes = [P, P, I64, I64, INT, P]
         getattr(lib, f).restype = INT
     for f in ("qmm_gemv", "qmm_gemm"):
@@ -133,6 +133,14 @@ def test_wka8_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 8, 64, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4096, 64, 3, 2048, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 16, 4000, 64, 8, 128, None) == INVALID
+
+
+def test_pack_signed_validation(lib):
+    f = lib.qmm_pack_signed
+    assert f(None, FAKE, 256, 8, 4, None) == INVALID
+    assert f(FAKE, None, 256, 8, 4, None) == INVALID
+    assert f(FAKE, FAKE, 256, 8, 0, None) == INVALID
+    assert f(FAKE, FAKE, 250, 8, 4, None) == INVALID
 
 
 def test_quantize_validation(lib):

@@ -476,3 +476,55 @@ def test_wka8_many_tiles(q, orc, bits):
     c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(94, bits), bits=bits, per_group_z=True)
     Y, acc = run_wka8(q, c, bits)
     check_wka8(orc, c, bits, Y, acc)
+
+
+# ---------------------------------------------------------- signed codes ---
+def signed_codes(bits, K, N, seed):
+    g = synthetic.rng(seed)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    q = g.integers(lo, hi + 1, (K, N))
+    q[0, :], q[1, :] = lo, hi
+    return q.astype(np.int8)
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_pack_signed(q, orc, bits):
+    K, N = 256, 37
+    qs = signed_codes(bits, K, N, 300 + bits)
+    wq = q.pack_signed(dev(qs), bits)
+    assert np.array_equal(stream_bytes(wq), orc.pack_signed(qs, bits))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("M", [1, 5, 40])
+def test_signed_codes_product(q, orc, bits, M):
+    """Signed codes with the default zero-point through qmm_gemv (M <= 16) or
+    qmm_gemm: Y = X (q s), checked against the oracle and against the numpy
+    closed form of the signed definition."""
+    K, N, G = 512, 70, 128
+    qs = signed_codes(bits, K, N, 310 + bits + M)
+    c = synthetic.make_case(M, K, N, bits, G, 320 + bits + M)
+    wq = q.pack_signed(dev(qs), bits)
+    fn = q.gemv if M <= 16 else q.gemm
+    Y = fn(dev(c["X"]), wq, dev(c["s"]), None, bits, G)
+    ref = orc.qmm(c["X"], orc.pack_signed(qs, bits), c["s"], None, bits, G)
+    direct = c["X"].astype(np.float64) @ (qs.astype(np.float64) * np.repeat(c["s"].astype(np.float64).T, G, axis=0))
+    assert np.abs(ref - direct).max() <= 1e-9 * np.abs(direct).max()
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_signed_codes_int8_activations(q, orc, bits):
+    """Signed codes on the int8-activation path: int32 group sums exact."""
+    M, K, N, G = 16, 1024, 50, 128
+    qs = signed_codes(bits, K, N, 330 + bits)
+    c = synthetic.make_w4a8_case(M, K, N, G, 340 + bits, bits=bits)
+    wq = q.pack_signed(dev(qs), bits)
+    acc = torch.zeros((M, K // G, N), dtype=torch.int32, device=DEV)
+    Y = q.gemm_wka8(dev(c["Xq"]), dev(c["sx"]), wq, dev(c["s"]), None, bits, G, acc_out=acc)
+    A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack_signed(qs, bits), c["s"], None, G, bits=bits)
+    direct = np.stack([c["Xq"][:, g * G:(g + 1) * G].astype(np.int64) @ qs[g * G:(g + 1) * G].astype(np.int64)
+                       for g in range(K // G)], axis=1)
+    assert np.array_equal(A, direct)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y, ref) <= TOL
