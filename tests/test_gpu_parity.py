@@ -528,3 +528,43 @@ def test_signed_codes_int8_activations(q, orc, bits):
     assert np.array_equal(A, direct)
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
     assert rel_err(Y, ref) <= TOL
+
+
+# ------------------------------------------------------ smallest shapes ---
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("M", [1, 2, 16, 17])
+@pytest.mark.parametrize("K,N,G", [(32, 1, 32), (128, 1, 128), (128, 3, 32)])
+def test_smallest_products(q, orc, bits, M, K, N, G):
+    """One run or one 128-row step, one to three columns: every product entry
+    point that takes the shape (qmm_gemv for M <= 16, qmm_gemm always).
+
+    With one or three outputs, max|Y| can be a small residue of cancelling
+    terms, and max|dY| / max|Y| is then ill-conditioned (the GEMM's one
+    rounding per weight is 2^-11 of each |x w| term).  The error is bounded
+    instead by 4e-3 of max(|X| |W|), which any indexing mistake (an error of
+    the size of the terms) still exceeds."""
+    c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(92, bits, M + K + N), per_group_z=True)
+    st = orc.pack(c["codes"], bits)
+    ref = orc.qmm(c["X"], st, c["s"], c["z"], bits, G)
+    scale = (np.abs(c["X"].astype(np.float64)) @ np.abs(orc.dequant(st, c["s"], c["z"], K, N, bits, G))).max()
+    fns = [q.gemm] + ([q.gemv] if M <= 16 else [])
+    for fn in fns:
+        Y = run_product(q, fn, c)
+        err = np.abs(Y.float().cpu().numpy().astype(np.float64) - ref).max()
+        assert err <= TOL * scale, (fn.__name__, err, scale)
+
+
+@pytest.mark.parametrize("bits", [1, 4, 8])
+@pytest.mark.parametrize("M,N", [(1, 1), (17, 3)])
+def test_smallest_int8_products(q, orc, bits, M, N):
+    """One 128-row group, one to three columns, on the int8-activation path."""
+    K, G = 128, 128
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(95, bits, M + N), bits=bits, per_group_z=True)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+
+
+@pytest.mark.parametrize("bits", [1, 4, 8])
+def test_smallest_quantize(q, orc, bits):
+    W = synthetic.fp16_normal(synthetic.rng(96 + bits), (32, 1))
+    check_quantize(q, orc, W, bits, 32)
