@@ -5,7 +5,7 @@ devices, passes raw device pointers and the current HIP stream to the C ABI
 (``include/qmm.h``) and raises :class:`QmmError` on a non-zero status.  Every
 step of the computation runs in the library's HIP kernels; there is no
 fallback.  Importing the package fails loudly if ``libqmm.so`` has not been
-built (``python -m bit_weight_quantized_qmm_amd._build``).
+built (``python bit_weight_quantized_qmm_amd/_build.py``).
 
 PyTorch is used for device memory and streams only.
 """
@@ -33,7 +33,7 @@ class QmmError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is missing: build it first (python -m bit_weight_quantized_qmm_amd._build)")
+        raise ImportError(f"{LIBRARY} is missing: build it first (python bit_weight_quantized_qmm_amd/_build.py)")
     lib = ctypes.CDLL(LIBRARY)
     P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sig = {

@@ -22,7 +22,12 @@ def declared_symbols():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        import bit_weight_quantized_qmm_amd._build as b
+        # by path: importing the package needs the library this builds
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "qmm_build", os.path.join(ROOT, "bit_weight_quantized_qmm_amd", "_build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     lib = ctypes.CDLL(LIB)
     P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
