@@ -64,6 +64,7 @@ class Oracle:
             "qmm_oracle_qmm_sampled": [_P, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P, _P, _I64, _P],
             "qmm_oracle_w4a8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P, _P],
             "qmm_oracle_quantize": [_P, _I64, _I64, _INT, _I64, _P, _P, _P],
+            "qmm_oracle_qmm_fp": [_P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -161,6 +162,26 @@ class Oracle:
         self._check(rc, "w4a8")
         return A, Y
 
+
+    FP_BITS = {0: 4, 1: 8}   # format -> code width: 0 = E2M1, 1 = E4M3
+
+    def float_code_value(self, q: int, fmt: int) -> float:
+        f = self.lib.qmm_oracle_float_code_value
+        f.argtypes = [ctypes.c_uint, _INT]
+        f.restype = ctypes.c_double
+        return f(q, fmt)
+
+    def qmm_fp(self, X, stream, s, fmt: int, G: int, N: int | None = None) -> np.ndarray:
+        """float64 Y = X . (value(q) * s) for floating-point codes (0: E2M1, 1: E4M3)."""
+        X64 = self._f64(X)
+        M, K = X64.shape
+        if N is None:
+            N = np.asarray(s).shape[0]
+        b = self._stream(stream, K, N, self.FP_BITS[fmt])
+        Y = np.zeros((M, N), dtype=np.float64)
+        self._check(self.lib.qmm_oracle_qmm_fp(_ptr(X64), _ptr(b), _ptr(self._f64(s)), M, K, N, fmt, G, _ptr(Y)),
+                    "qmm_fp")
+        return Y
 
     def quantize(self, W, bits: int, G: int):
         """(codes uint8 [K][N], s float16 [N][K/G], z float16 [N][K/G]) for fp16 W [K][N]."""

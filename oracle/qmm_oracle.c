@@ -38,6 +38,14 @@
  * widened exactly by the caller); z == NULL means z = 2^(k-1).  Group g of a
  * column covers rows [g*G, (g+1)*G).
  *
+ * Floating-point codes (qmm_oracle_qmm_fp): the Tilus verdict page lists
+ * float3..float8 weight types beside the integer ones without defining a
+ * format; the reading here is the two OCP 8-bit-and-below formats in common
+ * use: E2M1 (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * subnormal at exponent 0) and E4M3 (8 bits: sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; subnormal at exponent 0; the all-ones exponent and
+ * mantissa pattern is NaN, no infinities).  w = value(q) * s, no zero-point.
+ *
  * The quantiser (qmm_oracle_quantize) follows eq. (1) of the same section,
  * q = clip(round(w / s) + z, 0, 2^k - 1), with s and z chosen per (column,
  * group) from the group's range; its header states the reading.
@@ -288,4 +296,49 @@ int qmm_oracle_quantize(const double *W, int64_t K, int64_t N, int bits, int64_t
         }
     }
     return 0;
+}
+
+/* Value of a floating-point code: fmt 0 = E2M1 (4-bit), fmt 1 = E4M3 (8-bit),
+ * from the sign / exponent / mantissa fields as defined above. */
+static double float_code_value(unsigned q, int fmt)
+{
+    if (fmt == 0) {
+        const double sign = (q & 8u) ? -1.0 : 1.0;
+        const unsigned e = (q >> 1) & 3u, m = q & 1u;
+        return sign * (e == 0 ? ldexp((double)m, -1) : ldexp(1.0 + (double)m / 2.0, (int)e - 1));
+    }
+    const double sign = (q & 0x80u) ? -1.0 : 1.0;
+    const unsigned e = (q >> 3) & 15u, m = q & 7u;
+    if (e == 15 && m == 7) return NAN;
+    return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));
+}
+
+double qmm_oracle_float_code_value(unsigned q, int fmt) { return float_code_value(q, fmt); }
+
+/* Y = X . W with W[i][n] = value(q[i][n]) * s[n][i / G] for floating-point codes
+ * (fmt 0: E2M1 in 4-bit streams, fmt 1: E4M3 in 8-bit streams), fp64. */
+int qmm_oracle_qmm_fp(const double *X, const uint8_t *stream, const double *s, int64_t M, int64_t K, int64_t N,
+                      int fmt, int64_t G, double *Y)
+{
+    const int bits = fmt == 0 ? 4 : fmt == 1 ? 8 : 0;
+    if (!shape_ok(K, N, bits) || !groups_ok(K, G) || M < 0) return -1;
+    if ((M > 0 && N > 0) && (!Y || (K > 0 && (!X || !stream || !s)))) return -1;
+    const int64_t colbytes = K * bits / 8, ngroups = K / G;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *col = stream + n * colbytes;
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K ? K : 1));
+        if (!w) { failed = 1; continue; }
+        for (int64_t i = 0; i < K; ++i)
+            w[i] = float_code_value(column_code(col, i, bits), fmt) * s[n * ngroups + i / G];
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < K; ++i)
+                acc += X[m * K + i] * w[i];
+            Y[m * N + n] = acc;
+        }
+        free(w);
+    }
+    return failed ? -1 : 0;
 }

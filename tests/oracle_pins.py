@@ -310,6 +310,63 @@ def pin_signed_codes_dequantise_to_q_times_s(orc):
         assert np.array_equal(got, (q - z_rows) * s_rows), bits
 
 
+# ---------------------------------------------------- floating-point codes ---
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # the eight E2M1 magnitudes, codes 0..7
+
+
+def pin_e2m1_values(orc):
+    """E2M1 codes 0..7 are the eight magnitudes in order; bit 3 is the sign."""
+    for q in range(16):
+        v = orc.float_code_value(q, 0)
+        assert abs(v) == E2M1_MAGNITUDES[q & 7] and (np.signbit(v) == bool(q & 8)), q
+
+
+def pin_e4m3_landmarks(orc):
+    """E4M3 facts: 1.0 = 0x38, 2^-6 = 0x08 (smallest normal), 2^-9 = 0x01 (smallest
+    subnormal), 448 = 0x7E (largest), NaN only at 0x7F / 0xFF, bit 7 the sign,
+    magnitudes strictly increasing over 0x00..0x7E with 8 equal steps per binade
+    (steps of 2^-9 through the subnormals and the first normal binade)."""
+    v = [orc.float_code_value(q, 1) for q in range(256)]
+    assert v[0x38] == 1.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x7E] == 448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and sum(np.isnan(x) for x in v) == 2
+    for q in range(0x7F):
+        assert v[q + 0x80] == -v[q] and np.signbit(v[q + 0x80])
+    mags = v[:0x7F]
+    assert all(b > a for a, b in zip(mags, mags[1:]))
+    for q in range(0, 0x78, 8):   # each run of 8 codes has equal steps
+        steps = {mags[q + j + 1] - mags[q + j] for j in range(7)}
+        assert len(steps) == 1, q
+    assert mags[1] - mags[0] == 2.0 ** -9 and mags[9] - mags[8] == 2.0 ** -9
+
+
+def pin_float_code_product_bruteforce(orc):
+    """Y = X (value(q) s) for both formats against exact rational arithmetic
+    (E2M1 values from the magnitude table, E4M3 from the landmark-checked decode)."""
+    rng = np.random.default_rng(2200)
+    for fmt, bits in ((0, 4), (1, 8)):
+        M, K, N, G = 2, 64, 3, 32
+        hi = 16 if fmt == 0 else 256
+        codes = rng.integers(0, hi, (K, N))
+        if fmt == 1:
+            codes[(codes & 0x7F) == 0x7F] = 0x3A   # NaN codes are not inputs
+        X = rng.normal(0, 1, (M, K)).astype(np.float16)
+        s = rng.uniform(0.01, 0.1, (N, K // G)).astype(np.float16)
+        st = brute.bigint_pack(codes.astype(np.uint8), bits)
+        Y = orc.qmm_fp(X, st, s, fmt, G)
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(0)
+                aabs = Fraction(0)
+                for i in range(K):
+                    q = int(codes[i, n])
+                    val = (Fraction(E2M1_MAGNITUDES[q & 7]) * (-1 if q & 8 else 1)) if fmt == 0 else \
+                        Fraction(orc.float_code_value(q, 1))
+                    t = Fraction(float(X[m, i])) * val * Fraction(float(s[n, i // G]))
+                    exact += t
+                    aabs += abs(t)
+                assert abs(Fraction(Y[m, n]) - exact) <= brute.fp64_sum_bound(K, aabs) * 2, (fmt, m, n)
+
+
 # --------------------------------------------------------------- quantiser ---
 def _quantize_cases():
     """Tiny fp16 weight matrices with the special groups of the reading: random

@@ -63,6 +63,14 @@ MUTANTS = {
                                  "const double r = floor(x / quantum) * quantum;"),
     "quantize_scale_not_fp16": ("double sg = round_to_fp16((hi - lo) / qmax);",
                                 "double sg = (hi - lo) / qmax;"),
+    "e2m1_bias_off_by_one": ("return sign * (e == 0 ? ldexp((double)m, -1) : ldexp(1.0 + (double)m / 2.0, (int)e - 1));",
+                             "return sign * (e == 0 ? ldexp((double)m, -1) : ldexp(1.0 + (double)m / 2.0, (int)e));"),
+    "e4m3_no_subnormals": ("return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));",
+                           "return sign * (e == 0 ? ldexp(1.0 + (double)m / 8.0, -7) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));"),
+    "e4m3_mantissa_halved": ("return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));",
+                             "return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 16.0, (int)e - 7));"),
+    "fp_product_scale_dropped": ("w[i] = float_code_value(column_code(col, i, bits), fmt) * s[n * ngroups + i / G];",
+                                 "w[i] = float_code_value(column_code(col, i, bits), fmt);"),
     "sampled_drops_scale": ("            double w = (q - zero_point(z, n, g, ngroups, bits)) * s[n * ngroups + g];",
                             "            double w = (q - zero_point(z, n, g, ngroups, bits));"),
 }
