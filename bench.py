@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
@@ -248,6 +250,28 @@ def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
 
 
+def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
+    """qmm_gemm_fp on the prefill shape (M 2048, K = N = 4096, G 128) with E2M1
+    (fmt 0) or E4M3 (fmt 1) codes: TFLOP/s against the dense fp16 MFMA peak."""
+    w = synthetic.PREFILL
+    M, K, N, G = w["M"], w["K"], w["N"], w["G"]
+    bits = 4 if fmt == 0 else 8
+    g = synthetic.rng(synthetic.seed_for(4, bits, 11 + fmt))
+    codes = g.integers(0, 1 << bits, (K, N))
+    if fmt == 1:
+        codes[(codes & 0x7F) == 0x7F] = 0x30
+    wq = q.pack(torch.from_numpy(codes.astype(np.uint8)).to("cuda:0"), bits)
+    s = torch.from_numpy(synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G))).to("cuda:0")
+    X = torch.from_numpy(synthetic.fp16_normal(g, (M, K))).to("cuda:0")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    for _ in range(3):
+        q.gemm_fp(X, wq, s, fmt, G, out=Y)
+    ms = timer.region_ms(lambda i: q.gemm_fp(X, wq, s, fmt, G, out=Y), reps) / reps
+    tfs = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"workload": f"prefill-gemm {'E2M1' if fmt == 0 else 'E4M3'} codes M{M} K{K} N{N} G{G}",
+            "us": round(ms * 1e3, 2), "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
+
+
 def quantize_suite(torch, q, synthetic, timer, reps):
     """qmm_quantize on the 7B MLP weight (K 4096, N 11008, G 128, k 4): fp16 W in,
     codes, s and z out; HBM-bound."""
@@ -360,7 +384,9 @@ def main():
         suite = {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
                  "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
                  "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
-                 "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps)}
+                 "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps),
+                 "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
+                 "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1)}
 
     cpu = None
     if not args.no_cpu:

@@ -18,10 +18,11 @@ import torch
 
 from ._build import LIBRARY
 
-__all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemm", "gemm_w4a8", "gemm_wka8", "quantize",
+__all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemm", "gemm_fp", "FP4_E2M1",
+           "FP8_E4M3", "gemm_w4a8", "gemm_wka8", "quantize",
            "library_path", "SYMBOLS"]
 
-SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_w4a8", "qmm_gemm_wka8",
+SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_fp", "qmm_gemm_w4a8", "qmm_gemm_wka8",
            "qmm_quantize", "qmm_status_string", "qmm_last_error")
 
 
@@ -43,6 +44,7 @@ def _load():
         "qmm_unpack": ([P, P, I64, I64, INT, P], INT),
         "qmm_gemv": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_gemm_fp": ([P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm_w4a8": ([P, P, P, P, P, P, P, I64, I64, I64, I64, P], INT),
         "qmm_gemm_wka8": ([P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_quantize": ([P, P, P, P, I64, I64, INT, I64, P], INT),
@@ -148,6 +150,24 @@ def gemv(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
 def gemm(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
     """Y [M, N] fp16 = X [M, K] fp16 . dequant(wq); any M (f16 MFMA path)."""
     return _product(_lib.qmm_gemm, X, wq, s, z, bits, G, out)
+
+
+FP4_E2M1, FP8_E4M3 = 0, 1
+_FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8}
+
+
+def gemm_fp(X, wq, s, fmt: int, G: int, out=None) -> torch.Tensor:
+    """Y [M, N] fp16 = X . (value(q) s) for floating-point codes (FP4_E2M1 or FP8_E4M3)."""
+    _need(X, "X", torch.float16)
+    M, K = X.shape
+    N = s.shape[0]
+    _need(wq, "wq", torch.int32, (N, K * _FP_BITS.get(fmt, 0) // 32), X.device)
+    _need(s, "s", torch.float16, (N, K // G), X.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(out, "out", torch.float16, (M, N), X.device)
+    _check(_lib.qmm_gemm_fp(_ptr(X), _ptr(wq), _ptr(s), _ptr(out), M, K, N, fmt, G, _stream(X.device)))
+    return out
 
 
 def gemm_w4a8(Xq, sx, wq, s, z, G: int, out=None, acc_out=None) -> torch.Tensor:

@@ -115,6 +115,19 @@ qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
     return product("qmm_gemm", false, X, wq, s, z, Y, M, K, N, bits, G, stream);
 }
 
+qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s, qmm_half *Y, int64_t M, int64_t K,
+                       int64_t N, int fmt, int64_t G, qmm_stream stream)
+{
+    const char *fn = "qmm_gemm_fp";
+    if (fmt != QMM_FP4_E2M1 && fmt != QMM_FP8_E4M3) return fail(QMM_ERR_INVALID_ARG, "%s: unknown code format", fn);
+    const int bits = fmt == QMM_FP4_E2M1 ? 4 : 8;
+    qmm_status st = check_shape(fn, M, K, N, bits, G, true);
+    if (st != QMM_OK) return st;
+    if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    qmm::GemvArgs a{X, wq, s, nullptr, Y, (int)M, (int)K, (int)N, bits, (int)G};
+    return hip_status(qmm::launch_gemm_fp(a, fmt == QMM_FP4_E2M1 ? 0 : 1, (hipStream_t)stream), fn);
+}
+
 static qmm_status int8_product(const char *fn, const int8_t *Xq, const qmm_half *sx, const uint32_t *wq,
                                const qmm_half *s, const qmm_half *z, qmm_half *Y, int32_t *acc_out, int64_t M,
                                int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)

@@ -11,6 +11,13 @@
 // Workgroup tile 128 (M) x 256 (N), 4 waves side by side in N, wave tile
 // 128 x 64 = 8 x 4 MFMA tiles.  K advances 128 rows per step: lane group g
 // (lanes 16g..16g+15) of every MFMA owns run 4t+g.
+//
+// Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
+// streams; qmm_gemm_fp) keep the codes in order, so X is staged unpermuted.
+// A code's sign bit and magnitude bits, moved into an fp16 bit pattern
+// (magnitude at bit 9 for E2M1, bit 7 for E4M3), read as that fp16 number
+// times 2^-14 (E2M1) or 2^-8 (E4M3), subnormals included: one exact multiply
+// restores the value, a second applies s (one rounding).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -66,7 +73,7 @@ __device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &
 
 // Workgroup tile 128 (M) x 256 (N): 4 waves side by side in N, each 128 x 64
 // = 8 x 4 MFMA tiles, so every weight run is dequantised by exactly one lane.
-template <int BITS, bool PGZ>
+template <int BITS, bool PGZ, int FMT>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
@@ -113,7 +120,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             const int it = tid + 256 * i;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
-            x_slots_g<BITS>(raw[i], xs);
+            if constexpr (FMT == 0) {
+                x_slots_g<BITS>(raw[i], xs);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xs[j] = as_half2(raw[i][j]);   // codes in order
+            }
             uint8_t *dst = &lds[buf][row * GEMM_ROWB + gg * 64];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -167,6 +179,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
         half8_t bq[4][4];
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) {
+          if constexpr (FMT != 0) {
+            half2_t s2;
+            s2[0] = as_half(scur[ns]);
+            s2[1] = s2[0];
+            half2_t up;   // 2^14 (E2M1) or 2^8 (E4M3): exact
+            up[0] = (_Float16)(FMT == 1 ? 16384.0f : 256.0f);
+            up[1] = up[0];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                uint32_t hb;
+                if constexpr (FMT == 1) {   // codes 2j, 2j+1: the nibbles of byte j % 4 of dword j / 4
+                    const uint32_t t = dcur[ns][j >> 2] >> (8 * (j & 3));
+                    hb = ((t & 0x8u) << 12) | ((t & 0x7u) << 9) | ((t & 0x80u) << 24) | ((t & 0x70u) << 21);
+                } else {                    // codes 2j, 2j+1: bytes 2 (j % 2), + 1 of dword j / 2
+                    const uint32_t t = dcur[ns][j >> 1] >> (16 * (j & 1));
+                    hb = ((t & 0x80u) << 8) | ((t & 0x7fu) << 7) | ((t & 0x8000u) << 16) | ((t & 0x7f00u) << 15);
+                }
+                const half2_t w = (as_half2(hb) * up) * s2;
+                bq[ns][j >> 2][2 * (j & 3)] = w[0];
+                bq[ns][j >> 2][2 * (j & 3) + 1] = w[1];
+            }
+          } else {
             uint32_t h[16];
             run_to_half2<BITS>(dcur[ns], h);
             half2_t s2;
@@ -198,6 +232,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                     bq[ns][u][2 * e + 1] = w[1];
                 }
             }
+          }
         }
         const uint8_t *abase = abase0 + cur * (GEMM_BM * GEMM_ROWB);
         // All 32 A fragments of the step stay in registers while the MFMAs walk
@@ -243,33 +278,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     }
 }
 
-template <int BITS>
+template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
     const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + GEMM_BN - 1) / GEMM_BN;
     const dim3 block(256), grid((unsigned)(mtiles * ntiles));
-    if (a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K, a.N,
-                           a.G, mtiles, ntiles);
+    if (FMT == 0 && a.z)
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K,
+                           a.N, a.G, mtiles, ntiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K, a.N,
-                           a.G, mtiles, ntiles);
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K,
+                           a.N, a.G, mtiles, ntiles);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)
 {
     switch (a.bits) {
-        case 1: return gemm_dispatch<1>(a, st);
-        case 2: return gemm_dispatch<2>(a, st);
-        case 3: return gemm_dispatch<3>(a, st);
-        case 4: return gemm_dispatch<4>(a, st);
-        case 5: return gemm_dispatch<5>(a, st);
-        case 6: return gemm_dispatch<6>(a, st);
-        case 7: return gemm_dispatch<7>(a, st);
-        case 8: return gemm_dispatch<8>(a, st);
+        case 1: return gemm_dispatch<1, 0>(a, st);
+        case 2: return gemm_dispatch<2, 0>(a, st);
+        case 3: return gemm_dispatch<3, 0>(a, st);
+        case 4: return gemm_dispatch<4, 0>(a, st);
+        case 5: return gemm_dispatch<5, 0>(a, st);
+        case 6: return gemm_dispatch<6, 0>(a, st);
+        case 7: return gemm_dispatch<7, 0>(a, st);
+        case 8: return gemm_dispatch<8, 0>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Floating-point codes: fmt 0 = E2M1 (4-bit stream), fmt 1 = E4M3 (8-bit
+// stream); a.bits must match, a.z is ignored.
+hipError_t launch_gemm_fp(const GemvArgs &a, int fmt, hipStream_t st)
+{
+    if (fmt == 0 && a.bits == 4) return gemm_dispatch<4, 1>(a, st);
+    if (fmt == 1 && a.bits == 8) return gemm_dispatch<8, 2>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qmm

@@ -122,6 +122,24 @@ qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
                     qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
                     qmm_stream stream);
 
+/* Floating-point weight codes for qmm_gemm_fp (OCP field definitions: the
+ * reading of the Tilus verdict page's float3..float8 types, pith extraction,
+ * forward implications). */
+enum {
+    QMM_FP4_E2M1 = 0,   /* 4-bit stream: sign, 2 exponent bits (bias 1), 1 mantissa bit; 0..6 */
+    QMM_FP8_E4M3 = 1    /* 8-bit stream: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0..448,
+                           codes 0x7F / 0xFF (NaN) are not valid weights */
+};
+
+/* Y = X . W with W[k][n] = value(q[k][n]) * s[n][k / G] for floating-point codes
+ * (no zero-point), any M >= 1, on the qmm_gemm kernel: the code's sign and
+ * magnitude bits become an fp16 number scaled by an exact power of two, and
+ * one rounding multiply applies s.  wq is qmm_pack's stream of the code bit
+ * patterns at 4 bits (E2M1) or 8 bits (E4M3); X, s, Y, M, K, N, G, stream and
+ * the errors as for qmm_gemm; an unknown fmt gives QMM_ERR_INVALID_ARG. */
+qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s, qmm_half *Y, int64_t M,
+                       int64_t K, int64_t N, int fmt, int64_t G, qmm_stream stream);
+
 /* Integer-activation product with 4-bit weights (BitLLM Sec. 4.3 dp4a semantics,
  * Sec. 4.4 deferred dequantisation):
  *   A[m][g][n] = sum_{i in group g} Xq[m][i] * (q[i][n] - z[n][g])   (exact int32)

@@ -43,6 +43,8 @@ def lib():
     lib.qmm_gemm_w4a8.restype = INT
     lib.qmm_gemm_wka8.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P]
     lib.qmm_gemm_wka8.restype = INT
+    lib.qmm_gemm_fp.argtypes = [P, P, P, P, I64, I64, I64, INT, I64, P]
+    lib.qmm_gemm_fp.restype = INT
     lib.qmm_quantize.argtypes = [P, P, P, P, I64, I64, INT, I64, P]
     lib.qmm_quantize.restype = INT
     lib.qmm_status_string.argtypes = [INT]
@@ -146,6 +148,15 @@ def test_pack_signed_validation(lib):
     assert f(FAKE, None, 256, 8, 4, None) == INVALID
     assert f(FAKE, FAKE, 256, 8, 0, None) == INVALID
     assert f(FAKE, FAKE, 250, 8, 4, None) == INVALID
+
+
+def test_gemm_fp_validation(lib):
+    f = lib.qmm_gemm_fp
+    for fmt in (-1, 2, 7):
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 256, 8, fmt, 64, None) == INVALID
+    assert f(None, FAKE, FAKE, FAKE, 4, 256, 8, 0, 64, None) == INVALID
+    assert f(FAKE, FAKE, None, FAKE, 4, 256, 8, 1, 64, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 256, 8, 0, 48, None) == INVALID
 
 
 def test_quantize_validation(lib):

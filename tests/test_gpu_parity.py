@@ -568,3 +568,50 @@ def test_smallest_int8_products(q, orc, bits, M, N):
 def test_smallest_quantize(q, orc, bits):
     W = synthetic.fp16_normal(synthetic.rng(96 + bits), (32, 1))
     check_quantize(q, orc, W, bits, 32)
+
+
+# ------------------------------------------------- floating-point codes ---
+def fp_codes(fmt, K, N, seed):
+    g = synthetic.rng(seed)
+    if fmt == 0:
+        return g.integers(0, 16, (K, N)).astype(np.uint8)
+    q = g.integers(0, 256, (K, N))
+    q[(q & 0x7F) == 0x7F] = 0x30        # NaN patterns are not weights
+    return q.astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M", [1, 5, 130])
+@pytest.mark.parametrize("G", [64, 128])
+def test_gemm_fp_codes(q, orc, fmt, M, G):
+    """E2M1 and E4M3 codes through qmm_gemm_fp: several tiles, ragged M and N."""
+    K, N = 512, 300
+    bits = orc.FP_BITS[fmt]
+    codes = fp_codes(fmt, K, N, 400 + fmt + M + G)
+    c = synthetic.make_case(M, K, N, bits, G, 410 + fmt + M + G)
+    wq = q.pack(dev(codes), bits)
+    Y = q.gemm_fp(dev(c["X"]), wq, dev(c["s"]), fmt, G)
+    ref = orc.qmm_fp(c["X"], orc.pack(codes, bits), c["s"], fmt, G)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemm_fp_decodes_every_code_exactly(q, orc, fmt):
+    """One-hot rows of X read single weights back: Y = fp16(value(q) s) bit for bit
+    for every code (both signs, subnormals, the largest values)."""
+    bits = orc.FP_BITS[fmt]
+    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    K, G = 256, 128
+    N = 64
+    codes = np.zeros((K, N), dtype=np.uint8)
+    for idx, v in enumerate(allq):
+        codes[idx % K, idx // K * 8 + idx % 8] = v      # spread over rows and columns
+    M = K
+    X = np.eye(K, dtype=np.float16)
+    s = synthetic.fp16_uniform(synthetic.rng(420 + fmt), 0.5, 2.0, (N, K // G))
+    wq = q.pack(dev(codes), bits)
+    Y = q.gemm_fp(dev(X), wq, dev(s), fmt, G).cpu().numpy()
+    vals = np.array([[orc.float_code_value(int(codes[i, n]), fmt) for n in range(N)] for i in range(K)])
+    expect = (vals * np.repeat(s.astype(np.float64).T, G, axis=0)).astype(np.float16)
+    # values, not bit patterns: -0 (E2M1 code 8) times one, plus +0 products, sums to +0
+    assert np.array_equal(Y.astype(np.float64), expect.astype(np.float64))
