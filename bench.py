@@ -272,6 +272,38 @@ def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
             "us": round(ms * 1e3, 2), "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
 
 
+def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
+    """qmm_gemm_fp at M = 1 on the 7B MLP shape (K 4096, N 11008, G 128) with E2M1
+    (fmt 0) or E4M3 (fmt 1) codes: weights streamed from HBM (rotating copies)."""
+    w = synthetic.DECODE_7B
+    K, N, G = w["K"], w["N"], w["G"]
+    bits = 4 if fmt == 0 else 8
+    g = synthetic.rng(synthetic.seed_for(2, bits, 13 + fmt))
+    codes = g.integers(0, 1 << bits, (K, N))
+    if fmt == 1:
+        codes[(codes & 0x7F) == 0x7F] = 0x30
+    wq = q.pack(torch.from_numpy(codes.astype(np.uint8)).to("cuda:0"), bits)
+    s = torch.from_numpy(synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G))).to("cuda:0")
+    bufs = rotating(torch, (wq, s))
+    X = torch.from_numpy(synthetic.fp16_normal(g, (1, K))).to("cuda:0")
+    Y = torch.empty((1, N), dtype=torch.float16, device="cuda:0")
+
+    state = {"i": 0}
+
+    def launch(i):
+        b = bufs[state["i"] % len(bufs)]
+        state["i"] += 1
+        q.gemm_fp(X, b[0], b[1], fmt, G, out=Y)
+
+    for i in range(3):
+        launch(i)
+    ms = timer.region_ms(launch, reps) / reps
+    alg = K * N * bits // 8 + N * (K // G) * 2 + K * 2 + N * 2
+    return {"workload": f"decode {'E2M1' if fmt == 0 else 'E4M3'} codes 7B-MLP M1 K{K} N{N} G{G}",
+            "us": round(ms * 1e3, 2), "algorithmic_GBs": round(alg / ms / 1e6, 1),
+            "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def quantize_suite(torch, q, synthetic, timer, reps):
     """qmm_quantize on the 7B MLP weight (K 4096, N 11008, G 128, k 4): fp16 W in,
     codes, s and z out; HBM-bound."""
@@ -386,7 +418,9 @@ def main():
                  "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
                  "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps),
                  "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
-                 "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1)}
+                 "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1),
+                 "decode_fp4_e2m1": decode_fp_suite(torch, q, synthetic, timer, reps, 0),
+                 "decode_fp8_e4m3": decode_fp_suite(torch, q, synthetic, timer, reps, 1)}
 
     cpu = None
     if not args.no_cpu:

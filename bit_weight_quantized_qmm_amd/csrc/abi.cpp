@@ -125,7 +125,12 @@ qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s,
     if (st != QMM_OK) return st;
     if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
     qmm::GemvArgs a{X, wq, s, nullptr, Y, (int)M, (int)K, (int)N, bits, (int)G};
-    return hip_status(qmm::launch_gemm_fp(a, fmt == QMM_FP4_E2M1 ? 0 : 1, (hipStream_t)stream), fn);
+    const int f = fmt == QMM_FP4_E2M1 ? 0 : 1;
+    if (M == 1) {   // the decode kernel where it takes the shape
+        const hipError_t e = qmm::launch_gemv_fp(a, f, (hipStream_t)stream);
+        if (e != hipErrorNotSupported) return hip_status(e, fn);
+    }
+    return hip_status(qmm::launch_gemm_fp(a, f, (hipStream_t)stream), fn);
 }
 
 static qmm_status int8_product(const char *fn, const int8_t *Xq, const qmm_half *sx, const uint32_t *wq,

@@ -14,10 +14,8 @@
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
 // streams; qmm_gemm_fp) keep the codes in order, so X is staged unpermuted.
-// A code's sign bit and magnitude bits, moved into an fp16 bit pattern
-// (magnitude at bit 9 for E2M1, bit 7 for E4M3), read as that fp16 number
-// times 2^-14 (E2M1) or 2^-8 (E4M3), subnormals included: one exact multiply
-// restores the value, a second applies s (one rounding).
+// gfx950's packed fp4 / fp8 -> f16 conversions give two codes' exact values
+// per VALU op; one multiply applies s (one rounding).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -183,20 +181,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             half2_t s2;
             s2[0] = as_half(scur[ns]);
             s2[1] = s2[0];
-            half2_t up;   // 2^14 (E2M1) or 2^8 (E4M3): exact
-            up[0] = (_Float16)(FMT == 1 ? 16384.0f : 256.0f);
-            up[1] = up[0];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                uint32_t hb;
-                if constexpr (FMT == 1) {   // codes 2j, 2j+1: the nibbles of byte j % 4 of dword j / 4
-                    const uint32_t t = dcur[ns][j >> 2] >> (8 * (j & 3));
-                    hb = ((t & 0x8u) << 12) | ((t & 0x7u) << 9) | ((t & 0x80u) << 24) | ((t & 0x70u) << 21);
-                } else {                    // codes 2j, 2j+1: bytes 2 (j % 2), + 1 of dword j / 2
-                    const uint32_t t = dcur[ns][j >> 1] >> (16 * (j & 1));
-                    hb = ((t & 0x80u) << 8) | ((t & 0x7fu) << 7) | ((t & 0x8000u) << 16) | ((t & 0x7f00u) << 15);
-                }
-                const half2_t w = (as_half2(hb) * up) * s2;
+                const half2_t w = fp_code_pair<FMT>(dcur[ns], j) * s2;   // exact value, one rounding
                 bq[ns][j >> 2][2 * (j & 3)] = w[0];
                 bq[ns][j >> 2][2 * (j & 3) + 1] = w[1];
             }

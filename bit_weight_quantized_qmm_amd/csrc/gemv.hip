@@ -97,7 +97,7 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
     return v;
 }
 
-template <int BITS, int RPL, int D, int IPT, bool PGZ>
+template <int BITS, int RPL, int D, int IPT, bool PGZ, int FMT = 0>
 __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                       const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                       uint16_t *__restrict__ Y, int K, int N, int G)
@@ -171,10 +171,15 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
             const int it0 = tid + 256 * i;
             const int it = it0 < R ? it0 : R;        // R = the dummy item
             half2_t xs[16];
-            x_slots<BITS>(raw[i], xs);
             float a1 = 0.f, a2 = 0.f;
+            if constexpr (FMT != 0) {   // float codes: X in code order, no bias
 #pragma unroll
-            for (int p = 0; p < 16; ++p) {
+                for (int p = 0; p < 16; ++p) xs[p] = as_half2(raw[i][p]);
+            } else {
+                x_slots<BITS>(raw[i], xs);
+            }
+#pragma unroll
+            for (int p = 0; p < 16 && FMT == 0; ++p) {
                 if (PGZ) {
                     half2_t k1;
                     k1[0] = (_Float16)1024.0f;
@@ -225,15 +230,24 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
 #pragma unroll
                 for (int j = 0; j < RPL; ++j) {
                     uint32_t h[16];
-                    run_to_half2<BITS>(d[q][j], h);
+                    if constexpr (FMT != 0) {
+#pragma unroll
+                        for (int p = 0; p < 16; ++p) h[p] = as_u32(fp_code_pair<FMT>(d[q][j], p));
+                    } else {
+                        run_to_half2<BITS>(d[q][j], h);
+                    }
                     float a = 0.f, a_odd = 0.f;
 #pragma unroll
                     for (int p = 0; p < 16; p += 2) {
                         a = __builtin_amdgcn_fdot2(xv[j][p], as_half2(h[p]), a, false);
                         a_odd = __builtin_amdgcn_fdot2(xv[j][p + 1], as_half2(h[p + 1]), a_odd, false);
                     }
-                    const float bias = PGZ ? fmaf((float)as_half(zv[q][j]), b2[j], b1[j]) : b1[j];
-                    y = fmaf((float)as_half(sv[q][j]), (a + a_odd) - bias, y);
+                    if constexpr (FMT != 0) {   // exact code values: no bias
+                        y = fmaf((float)as_half(sv[q][j]), a + a_odd, y);
+                    } else {
+                        const float bias = PGZ ? fmaf((float)as_half(zv[q][j]), b2[j], b1[j]) : b1[j];
+                        y = fmaf((float)as_half(sv[q][j]), (a + a_odd) - bias, y);
+                    }
                 }
                 issue(q, i + D);                      // refill this slot (zeros past the wave's columns)
                 y = wave_sum_dpp(y);
@@ -858,19 +872,19 @@ static int num_cus()
 
 static int m1_grid(int N) { return std::max(1, std::min(num_cus(), (N + 3) / 4)); }
 
-template <int BITS, int RPL, int D, int IPT, bool PGZ>
+template <int BITS, int RPL, int D, int IPT, bool PGZ, int FMT = 0>
 static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
 {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_m1_kernel<BITS, RPL, D, IPT, PGZ>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_m1_kernel<BITS, RPL, D, IPT, PGZ, FMT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const size_t lds = m1_lds_bytes(a.K, PGZ);
     const dim3 block(256), grid(m1_grid(a.N));
-    hipLaunchKernelGGL((gemv_m1_kernel<BITS, RPL, D, IPT, PGZ>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y, a.K,
+    hipLaunchKernelGGL((gemv_m1_kernel<BITS, RPL, D, IPT, PGZ, FMT>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y, a.K,
                        a.N, a.G);
     return hipGetLastError();
 }
@@ -987,6 +1001,29 @@ static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
         }
     }
     return a.z ? gemv_mfma_launch<BITS, true>(a, st) : gemv_mfma_launch<BITS, false>(a, st);
+}
+
+// Floating-point codes at M = 1 (FMT 1: E2M1, 2: E4M3; no zero-point):
+// hipErrorNotSupported outside the decode kernel's shapes.
+template <int BITS, int FMT>
+static hipError_t gemv_m1_fp(const GemvArgs &a, hipStream_t st)
+{
+    const int R = a.K / 32;
+    if (!(a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
+          (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64))
+        return hipErrorNotSupported;
+    const int rpl_need = (R + 63) / 64;
+    if (rpl_need <= 1) return gemv_m1_go<BITS, 1, 8, 1, false, FMT>(a, st);
+    if (rpl_need <= 2) return gemv_m1_go<BITS, 2, 4, 1, false, FMT>(a, st);
+    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, 2, 1, false, FMT>(a, st);
+    return gemv_m1_go<BITS, 8, 1, 2, false, FMT>(a, st);
+}
+
+hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st)
+{
+    if (fmt == 0 && a.bits == 4) return gemv_m1_fp<4, 1>(a, st);
+    if (fmt == 1 && a.bits == 8) return gemv_m1_fp<8, 2>(a, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st)

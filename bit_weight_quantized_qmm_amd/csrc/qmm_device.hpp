@@ -95,6 +95,30 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
+// streams): codes 2j and 2j + 1 of a run d as an fp16 pair holding their exact
+// values, by gfx950's packed fp4 / fp8 -> f16 conversions at unit scale (one
+// VALU op per pair).  Every E2M1 value and every finite E4M3 value is zero or
+// an fp16 normal number.  The byte / word select is an immediate: j must be a
+// constant after unrolling.
+template <int FMT>
+__device__ __forceinline__ half2_t fp_code_pair(const uint32_t *d, int j)
+{
+    if constexpr (FMT == 1) {   // byte j % 4 of dword j / 4: low nibble first
+        const uint32_t w = d[j >> 2];
+        switch (j & 3) {
+            case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+            case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+            case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+            default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+        }
+    } else {                    // 16-bit word j % 2 of dword j / 2: low byte first
+        const uint32_t w = d[j >> 1];
+        return (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    }
+}
+
 // fp32 -> fp16 round to nearest even (v_cvt_f16_f32).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((_Float16)v); }
 

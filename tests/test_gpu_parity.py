@@ -596,6 +596,41 @@ def test_gemm_fp_codes(q, orc, fmt, M, G):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("K,N,G", [(32, 7, 32), (1056, 301, 32), (4096, 11008, 128), (16384, 515, 256),
+                                   (16416, 64, 32)])
+def test_gemm_fp_decode_shapes(q, orc, fmt, K, N, G):
+    """M = 1 float-code products: one run, a ragged run count, the 7B MLP decode
+    shape, the longest K the decode kernel takes and one past it."""
+    bits = orc.FP_BITS[fmt]
+    codes = fp_codes(fmt, K, N, 430 + fmt + K)
+    c = synthetic.make_case(1, K, N, bits, G, 440 + fmt + K)
+    wq = q.pack(dev(codes), bits)
+    Y = q.gemm_fp(dev(c["X"]), wq, dev(c["s"]), fmt, G)
+    ref = orc.qmm_fp(c["X"], orc.pack(codes, bits), c["s"], fmt, G)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
+    """M = 1, X one-hot at row i: Y[n] = fp16(value(q[i, n]) s) for every code,
+    each in its own column, at a row in the middle of a run and of a group."""
+    bits = orc.FP_BITS[fmt]
+    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    K, G = 512, 128
+    N = len(allq)
+    s = synthetic.fp16_uniform(synthetic.rng(450 + fmt), 0.5, 2.0, (N, K // G))
+    for i in (0, 45, 511):
+        codes = np.asarray(synthetic.rng(460 + i).integers(0, 16, (K, N)), dtype=np.uint8)
+        codes[i, :] = allq
+        X = np.zeros((1, K), dtype=np.float16)
+        X[0, i] = 1.0
+        Y = q.gemm_fp(dev(X), q.pack(dev(codes), bits), dev(s), fmt, G).cpu().numpy()
+        vals = np.array([orc.float_code_value(int(v), fmt) for v in allq])
+        expect = (vals * s[:, i // G].astype(np.float64)).astype(np.float16)
+        assert np.array_equal(Y[0].astype(np.float64), expect.astype(np.float64)), i
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_gemm_fp_decodes_every_code_exactly(q, orc, fmt):
     """One-hot rows of X read single weights back: Y = fp16(value(q) s) bit for bit
     for every code (both signs, subnormals, the largest values)."""
