@@ -596,11 +596,12 @@ def test_gemm_fp_codes(q, orc, fmt, M, G):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("K,N,G", [(32, 7, 32), (1056, 301, 32), (4096, 11008, 128), (16384, 515, 256),
-                                   (16416, 64, 32)])
+@pytest.mark.parametrize("K,N,G", [(32, 7, 32), (1056, 301, 32), (4096, 11008, 128), (8192, 1000, 128),
+                                   (16384, 515, 256), (16416, 64, 32)])
 def test_gemm_fp_decode_shapes(q, orc, fmt, K, N, G):
     """M = 1 float-code products: one run, a ragged run count, the 7B MLP decode
-    shape, the longest K the decode kernel takes and one past it."""
+    shape (2 runs per lane), 4 and 8 runs per lane (the longest K the decode
+    kernel takes) and one run past it (the GEMM kernel)."""
     bits = orc.FP_BITS[fmt]
     codes = fp_codes(fmt, K, N, 430 + fmt + K)
     c = synthetic.make_case(1, K, N, bits, G, 440 + fmt + K)
