@@ -273,8 +273,9 @@ def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
 
 
 def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
-    """qmm_gemm_fp at M = 1 on the 7B MLP shape (K 4096, N 11008, G 128) with E2M1
-    (fmt 0) or E4M3 (fmt 1) codes: weights streamed from HBM (rotating copies)."""
+    """qmm_gemm_fp at M = 1, 8, 16 on the 7B MLP shape (K 4096, N 11008, G 128)
+    with E2M1 (fmt 0) or E4M3 (fmt 1) codes: weights streamed from HBM
+    (rotating copies); HBM GB/s of the algorithmic bytes."""
     w = synthetic.DECODE_7B
     K, N, G = w["K"], w["N"], w["G"]
     bits = 4 if fmt == 0 else 8
@@ -285,23 +286,25 @@ def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
     wq = q.pack(torch.from_numpy(codes.astype(np.uint8)).to("cuda:0"), bits)
     s = torch.from_numpy(synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G))).to("cuda:0")
     bufs = rotating(torch, (wq, s))
-    X = torch.from_numpy(synthetic.fp16_normal(g, (1, K))).to("cuda:0")
-    Y = torch.empty((1, N), dtype=torch.float16, device="cuda:0")
+    X = torch.from_numpy(synthetic.fp16_normal(g, (16, K))).to("cuda:0")
+    out = {"workload": f"decode {'E2M1' if fmt == 0 else 'E4M3'} codes 7B-MLP K{K} N{N} G{G}"}
+    for M in (1, 8, 16):
+        x = X[:M].contiguous()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+        state = {"i": 0}
 
-    state = {"i": 0}
+        def launch(i, x=x, Y=Y, state=state):
+            b = bufs[state["i"] % len(bufs)]
+            state["i"] += 1
+            q.gemm_fp(x, b[0], b[1], fmt, G, out=Y)
 
-    def launch(i):
-        b = bufs[state["i"] % len(bufs)]
-        state["i"] += 1
-        q.gemm_fp(X, b[0], b[1], fmt, G, out=Y)
-
-    for i in range(3):
-        launch(i)
-    ms = timer.region_ms(launch, reps) / reps
-    alg = K * N * bits // 8 + N * (K // G) * 2 + K * 2 + N * 2
-    return {"workload": f"decode {'E2M1' if fmt == 0 else 'E4M3'} codes 7B-MLP M1 K{K} N{N} G{G}",
-            "us": round(ms * 1e3, 2), "algorithmic_GBs": round(alg / ms / 1e6, 1),
-            "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        for i in range(3):
+            launch(i)
+        ms = timer.region_ms(launch, reps) / reps
+        alg = K * N * bits // 8 + N * (K // G) * 2 + M * K * 2 + M * N * 2
+        out[f"M{M}"] = {"us": round(ms * 1e3, 2), "algorithmic_GBs": round(alg / ms / 1e6, 1),
+                        "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def quantize_suite(torch, q, synthetic, timer, reps):

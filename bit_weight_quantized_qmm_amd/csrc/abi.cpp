@@ -126,7 +126,7 @@ qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s,
     if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
     qmm::GemvArgs a{X, wq, s, nullptr, Y, (int)M, (int)K, (int)N, bits, (int)G};
     const int f = fmt == QMM_FP4_E2M1 ? 0 : 1;
-    if (M == 1) {   // the decode kernel where it takes the shape
+    if (M <= 16) {   // the decode kernels where they take the shape
         const hipError_t e = qmm::launch_gemv_fp(a, f, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e, fn);
     }

@@ -597,6 +597,8 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 // split into fp16 high and low parts and whose B fragment carries -1024 and
 // -z; then y += s * acc (BitLLM Sec. 2.2, eq. (5): w = (q - z) s, factored so
 // that the code-independent parts are applied once per step and group).
+// Floating-point codes (FMT != 0): A is X in code order and B the codes'
+// exact values from the packed fp4 / fp8 conversions; there is no correction.
 //
 // A workgroup of 8 waves owns tpw <= T consecutive 16-column tiles; wave w
 // owns K steps w*S .. w*S + S - 1 of every tile and keeps the A fragments of
@@ -612,7 +614,7 @@ static int num_cus();
 constexpr int MMA_WAVES = 8;   // waves per workgroup of the M <= 16 MFMA GEMV
 constexpr int MMA_MAXNG = 64;  // groups per column: K <= 8192, G >= 128
 
-template <int BITS, int S, int T, int D, bool PGZ>
+template <int BITS, int S, int T, int D, bool PGZ, int FMT = 0>
 __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                        const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                        uint16_t *__restrict__ Y, int M, int K, int N, int G, int tpw)
@@ -689,13 +691,18 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
         for (int st = 0; st < S; ++st) {
             half2_t xs[16];
-            x_slots<BITS>(xa[st], xs);
+            if constexpr (FMT != 0) {   // float codes: X in code order, no correction
+#pragma unroll
+                for (int p = 0; p < 16; ++p) xs[p] = as_half2(xa[st][p]);
+            } else {
+                x_slots<BITS>(xa[st], xs);
+            }
             half2_t one2;
             one2[0] = (_Float16)1.0f;
             one2[1] = (_Float16)1.0f;
             float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-            for (int p = 0; p < 16; ++p) {
+            for (int p = 0; p < 16 && FMT == 0; ++p) {
                 s1 = __builtin_amdgcn_fdot2(xs[p], one2, s1, false);
                 s2 = __builtin_amdgcn_fdot2(as_half2(xa[st][p]), one2, s2, false);
             }
@@ -738,7 +745,12 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                 const int t = wave * S + st;
                 const uint32_t szv = sz[min((t * 128) / G, ng - 1) * SZW + 16 * j + c];
                 uint32_t h[16];
-                run_to_half2<BITS>(d[slot], h);
+                if constexpr (FMT != 0) {
+#pragma unroll
+                    for (int p = 0; p < 16; ++p) h[p] = as_u32(fp_code_pair<FMT>(d[slot], p));
+                } else {
+                    run_to_half2<BITS>(d[slot], h);
+                }
                 half8_t bc;
                 {
                     const _Float16 zero = (_Float16)0.0f;
@@ -781,7 +793,8 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                     ac[6] = zero;
                     ac[7] = zero;
                 }
-                float4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac, bc, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (FMT == 0) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac, bc, acc, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st][u], b[u], acc, 0, 0, 0);
                 // refill the slot with the unit D ahead (past the tiles: no load)
@@ -812,29 +825,29 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 // N 28672) at M = 8 and 16 (wider codes leave fewer free registers).
 __host__ __device__ constexpr int mma_ring(int bits) { return bits <= 3 || bits == 7 ? 8 : bits == 8 ? 2 : 4; }
 
-template <int BITS, int S, int T, bool PGZ>
+template <int BITS, int S, int T, bool PGZ, int FMT>
 static hipError_t gemv_mma_go(const GemvArgs &a, int grid, int tpw, hipStream_t st)
 {
     constexpr int D0 = mma_ring(BITS);
     constexpr int D = D0 < S * T ? D0 : S * T;
-    hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
+    hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ, FMT>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
                        a.M, a.K, a.N, a.G, tpw);
     return hipGetLastError();
 }
 
-template <int BITS, int S, bool PGZ>
+template <int BITS, int S, bool PGZ, int FMT>
 static hipError_t gemv_mma_pick_t(const GemvArgs &a, int grid, int tpw, hipStream_t st)
 {
-    if (tpw <= 1) return gemv_mma_go<BITS, S, 1, PGZ>(a, grid, tpw, st);
-    if (tpw <= 2) return gemv_mma_go<BITS, S, 2, PGZ>(a, grid, tpw, st);
-    if (tpw <= 4) return gemv_mma_go<BITS, S, 4, PGZ>(a, grid, tpw, st);
-    return gemv_mma_go<BITS, S, 8, PGZ>(a, grid, tpw, st);
+    if (tpw <= 1) return gemv_mma_go<BITS, S, 1, PGZ, FMT>(a, grid, tpw, st);
+    if (tpw <= 2) return gemv_mma_go<BITS, S, 2, PGZ, FMT>(a, grid, tpw, st);
+    if (tpw <= 4) return gemv_mma_go<BITS, S, 4, PGZ, FMT>(a, grid, tpw, st);
+    return gemv_mma_go<BITS, S, 8, PGZ, FMT>(a, grid, tpw, st);
 }
 
 // Requires G % 128 == 0 and K <= 8192 (8 waves x 8 steps of 128 rows).  One
 // batch of at most 8 tiles per workgroup; past 8 x (CU count) tiles the
 // workgroups run in several rounds.
-template <int BITS, bool PGZ>
+template <int BITS, bool PGZ, int FMT = 0>
 static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
 {
     const int TT = (a.K / 32 + 3) / 4;                   // 128-row steps
@@ -842,10 +855,10 @@ static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
     const int tiles = (a.N + 15) / 16;
     const int tpw = std::min(8, std::max(1, (tiles + num_cus() - 1) / num_cus()));
     const int grid = (tiles + tpw - 1) / tpw;
-    if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ>(a, grid, tpw, st);
-    if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ>(a, grid, tpw, st);
-    if (steps <= 4) return gemv_mma_pick_t<BITS, 4, PGZ>(a, grid, tpw, st);
-    return gemv_mma_pick_t<BITS, 8, PGZ>(a, grid, tpw, st);
+    if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ, FMT>(a, grid, tpw, st);
+    if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ, FMT>(a, grid, tpw, st);
+    if (steps <= 4) return gemv_mma_pick_t<BITS, 4, PGZ, FMT>(a, grid, tpw, st);
+    return gemv_mma_pick_t<BITS, 8, PGZ, FMT>(a, grid, tpw, st);
 }
 
 static size_t m1_lds_bytes(int K, bool pgz)
@@ -1003,12 +1016,15 @@ static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
     return a.z ? gemv_mfma_launch<BITS, true>(a, st) : gemv_mfma_launch<BITS, false>(a, st);
 }
 
-// Floating-point codes at M = 1 (FMT 1: E2M1, 2: E4M3; no zero-point):
-// hipErrorNotSupported outside the decode kernel's shapes.
+// Floating-point codes (FMT 1: E2M1, 2: E4M3; no zero-point) at M = 1 on the
+// decode kernel and at 2 <= M <= 16 on the MFMA GEMV: hipErrorNotSupported
+// outside their shapes.
 template <int BITS, int FMT>
-static hipError_t gemv_m1_fp(const GemvArgs &a, hipStream_t st)
+static hipError_t gemv_small_fp(const GemvArgs &a, hipStream_t st)
 {
     const int R = a.K / 32;
+    if (a.M >= 2 && a.M <= 16 && a.G % 128 == 0 && a.K <= 64 * 128 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
+        return gemv_mma_launch<BITS, false, FMT>(a, st);
     if (!(a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
           (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64))
         return hipErrorNotSupported;
@@ -1021,8 +1037,8 @@ static hipError_t gemv_m1_fp(const GemvArgs &a, hipStream_t st)
 
 hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st)
 {
-    if (fmt == 0 && a.bits == 4) return gemv_m1_fp<4, 1>(a, st);
-    if (fmt == 1 && a.bits == 8) return gemv_m1_fp<8, 2>(a, st);
+    if (fmt == 0 && a.bits == 4) return gemv_small_fp<4, 1>(a, st);
+    if (fmt == 1 && a.bits == 8) return gemv_small_fp<8, 2>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -31,7 +31,7 @@ hipError_t launch_unpack(const uint32_t *wq, uint8_t *codes, int K, int N, int b
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st);
 hipError_t launch_gemm_fp(const GemvArgs &a, int fmt, hipStream_t st);
-hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st);   // M = 1; NotSupported otherwise
+hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st);   // M <= 16; NotSupported otherwise
 hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st);
 hipError_t launch_quantize(const uint16_t *W, uint8_t *codes, uint16_t *s, uint16_t *z, int K, int N, int bits, int G,
                            hipStream_t st);

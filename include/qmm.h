@@ -134,9 +134,11 @@ enum {
 /* Y = X . W with W[k][n] = value(q[k][n]) * s[n][k / G] for floating-point codes
  * (no zero-point), any M >= 1: gfx950's fp4 / fp8 -> f16 conversions give the
  * codes' exact values.  At M = 1 with K <= 16384, N <= 65536 the decode kernel runs (fp32
- * dot products of X with the values, s applied per group in fp32); otherwise
- * the qmm_gemm kernel (one rounding multiply by s, then f16 MFMA with fp32
- * accumulation).  wq is qmm_pack's stream of the code bit
+ * dot products of X with the values, s applied per group in fp32); at
+ * 2 <= M <= 16 with G % 128 == 0, K <= 8192 the MFMA GEMV (f16 MFMA of X with
+ * the values, fp32 accumulation, s applied per 128-row step in fp32);
+ * otherwise the qmm_gemm kernel (one rounding multiply by s, then f16 MFMA
+ * with fp32 accumulation).  wq is qmm_pack's stream of the code bit
  * patterns at 4 bits (E2M1) or 8 bits (E4M3); X, s, Y, M, K, N, G, stream and
  * the errors as for qmm_gemm; an unknown fmt gives QMM_ERR_INVALID_ARG. */
 qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s, qmm_half *Y, int64_t M,

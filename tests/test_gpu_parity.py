@@ -632,6 +632,44 @@ def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,K,N,G", [(2, 128, 17, 128), (8, 4096, 11008, 128), (16, 8192, 1000, 256),
+                                     (3, 1024, 300, 1024), (16, 8320, 40, 128)])
+def test_gemm_fp_batched_shapes(q, orc, fmt, M, K, N, G):
+    """2 <= M <= 16 float-code products: one 128-row step with a ragged tile,
+    the 7B MLP shape at M 8, the longest K the MFMA GEMV takes, one group per
+    column, and K past it (the GEMM kernel)."""
+    bits = orc.FP_BITS[fmt]
+    codes = fp_codes(fmt, K, N, 470 + fmt + K + M)
+    c = synthetic.make_case(M, K, N, bits, G, 480 + fmt + K + M)
+    wq = q.pack(dev(codes), bits)
+    Y = q.gemm_fp(dev(c["X"]), wq, dev(c["s"]), fmt, G)
+    ref = orc.qmm_fp(c["X"], orc.pack(codes, bits), c["s"], fmt, G)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemm_fp_batched_reads_every_code_exactly(q, orc, fmt):
+    """M = 16, row m of X one-hot at a different row i_m (even and odd code
+    positions, run and group boundaries): Y[m][n] = fp16(value(q[i_m][n]) s)."""
+    bits = orc.FP_BITS[fmt]
+    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    K, G = 512, 128
+    N = len(allq)
+    rows = [0, 1, 13, 31, 32, 45, 127, 128, 255, 256, 300, 383, 400, 450, 500, 511]
+    codes = np.asarray(synthetic.rng(490 + fmt).integers(0, 16, (K, N)), dtype=np.uint8)
+    X = np.zeros((16, K), dtype=np.float16)
+    for m, i in enumerate(rows):
+        codes[i, :] = np.roll(allq, 3 * m)
+        X[m, i] = 1.0
+    s = synthetic.fp16_uniform(synthetic.rng(495 + fmt), 0.5, 2.0, (N, K // G))
+    Y = q.gemm_fp(dev(X), q.pack(dev(codes), bits), dev(s), fmt, G).cpu().numpy()
+    for m, i in enumerate(rows):
+        vals = np.array([orc.float_code_value(int(v), fmt) for v in codes[i]])
+        expect = (vals * s[:, i // G].astype(np.float64)).astype(np.float16)
+        assert np.array_equal(Y[m].astype(np.float64), expect.astype(np.float64)), (m, i)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_gemm_fp_decodes_every_code_exactly(q, orc, fmt):
     """One-hot rows of X read single weights back: Y = fp16(value(q) s) bit for bit
     for every code (both signs, subnormals, the largest values)."""
