@@ -163,7 +163,7 @@ class Oracle:
         return A, Y
 
 
-    FP_BITS = {0: 4, 1: 8}   # format -> code width: 0 = E2M1, 1 = E4M3
+    FP_BITS = {0: 4, 1: 8, 2: 6, 3: 6}   # format -> code width: E2M1, E4M3, E3M2, E2M3
 
     def float_code_value(self, q: int, fmt: int) -> float:
         f = self.lib.qmm_oracle_float_code_value

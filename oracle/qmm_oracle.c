@@ -44,7 +44,10 @@
  * use: E2M1 (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa bit;
  * subnormal at exponent 0) and E4M3 (8 bits: sign, 4 exponent bits with bias
  * 7, 3 mantissa bits; subnormal at exponent 0; the all-ones exponent and
- * mantissa pattern is NaN, no infinities).  w = value(q) * s, no zero-point.
+ * mantissa pattern is NaN, no infinities), and at 6 bits the two OCP FP6
+ * formats, E3M2 (3 exponent bits with bias 3, 2 mantissa bits) and E2M3
+ * (2 exponent bits with bias 1, 3 mantissa bits), both with subnormals at
+ * exponent 0 and every code finite.  w = value(q) * s, no zero-point.
  *
  * The quantiser (qmm_oracle_quantize) follows eq. (1) of the same section,
  * q = clip(round(w / s) + z, 0, 2^k - 1), with s and z chosen per (column,
@@ -299,13 +302,21 @@ int qmm_oracle_quantize(const double *W, int64_t K, int64_t N, int bits, int64_t
 }
 
 /* Value of a floating-point code: fmt 0 = E2M1 (4-bit), fmt 1 = E4M3 (8-bit),
- * from the sign / exponent / mantissa fields as defined above. */
+ * fmt 2 = E3M2 and fmt 3 = E2M3 (6-bit), from the sign / exponent / mantissa
+ * fields as defined above. */
 static double float_code_value(unsigned q, int fmt)
 {
     if (fmt == 0) {
         const double sign = (q & 8u) ? -1.0 : 1.0;
         const unsigned e = (q >> 1) & 3u, m = q & 1u;
         return sign * (e == 0 ? ldexp((double)m, -1) : ldexp(1.0 + (double)m / 2.0, (int)e - 1));
+    }
+    if (fmt == 2 || fmt == 3) {
+        const int mb = fmt == 2 ? 2 : 3, bias = fmt == 2 ? 3 : 1;
+        const double sign = (q & 0x20u) ? -1.0 : 1.0;
+        const unsigned e = (q & 0x1fu) >> mb, m = q & ((1u << mb) - 1u);
+        const double frac = ldexp((double)m, -mb);
+        return sign * (e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, (int)e - bias));
     }
     const double sign = (q & 0x80u) ? -1.0 : 1.0;
     const unsigned e = (q >> 3) & 15u, m = q & 7u;
@@ -316,11 +327,12 @@ static double float_code_value(unsigned q, int fmt)
 double qmm_oracle_float_code_value(unsigned q, int fmt) { return float_code_value(q, fmt); }
 
 /* Y = X . W with W[i][n] = value(q[i][n]) * s[n][i / G] for floating-point codes
- * (fmt 0: E2M1 in 4-bit streams, fmt 1: E4M3 in 8-bit streams), fp64. */
+ * (fmt 0: E2M1 in 4-bit streams, fmt 1: E4M3 in 8-bit streams, fmt 2 / 3:
+ * E3M2 / E2M3 in 6-bit streams), fp64. */
 int qmm_oracle_qmm_fp(const double *X, const uint8_t *stream, const double *s, int64_t M, int64_t K, int64_t N,
                       int fmt, int64_t G, double *Y)
 {
-    const int bits = fmt == 0 ? 4 : fmt == 1 ? 8 : 0;
+    const int bits = fmt == 0 ? 4 : fmt == 1 ? 8 : (fmt == 2 || fmt == 3) ? 6 : 0;
     if (!shape_ok(K, N, bits) || !groups_ok(K, G) || M < 0) return -1;
     if ((M > 0 && N > 0) && (!Y || (K > 0 && (!X || !stream || !s)))) return -1;
     const int64_t colbytes = K * bits / 8, ngroups = K / G;

@@ -339,13 +339,41 @@ def pin_e4m3_landmarks(orc):
     assert mags[1] - mags[0] == 2.0 ** -9 and mags[9] - mags[8] == 2.0 ** -9
 
 
+def _fp6_landmarks(v, one, min_normal, min_sub, max_code, max_val, per_binade):
+    assert v[one] == 1.0 and v[per_binade] == min_normal and v[1] == min_sub and v[max_code] == max_val
+    assert not any(np.isnan(x) or np.isinf(x) for x in v)     # every code finite
+    for q in range(32):
+        assert v[q + 0x20] == -v[q] and np.signbit(v[q + 0x20])
+    mags = v[:32]
+    assert all(b > a for a, b in zip(mags, mags[1:]))
+    for q in range(0, 32, per_binade):   # equal steps inside each binade
+        assert len({mags[q + j + 1] - mags[q + j] for j in range(per_binade - 1)}) == 1, q
+    # subnormals continue the first normal binade's step
+    assert mags[1] - mags[0] == min_sub and mags[per_binade + 1] - mags[per_binade] == min_sub
+
+
+def pin_e3m2_landmarks(orc):
+    """E3M2 (6-bit, bias 3): 1.0 = 0x0C, 0.25 = 0x04 (smallest normal),
+    0.0625 = 0x01 (smallest subnormal), 28 = 0x1F (largest), bit 5 the sign,
+    4 codes per binade, every code finite."""
+    _fp6_landmarks([orc.float_code_value(q, 2) for q in range(64)], 0x0C, 0.25, 0.0625, 0x1F, 28.0, 4)
+
+
+def pin_e2m3_landmarks(orc):
+    """E2M3 (6-bit, bias 1): 1.0 = 0x08 (smallest normal), 0.125 = 0x01
+    (smallest subnormal), 7.5 = 0x1F (largest), bit 5 the sign, 8 codes per
+    binade, every code finite."""
+    _fp6_landmarks([orc.float_code_value(q, 3) for q in range(64)], 0x08, 1.0, 0.125, 0x1F, 7.5, 8)
+
+
 def pin_float_code_product_bruteforce(orc):
-    """Y = X (value(q) s) for both formats against exact rational arithmetic
-    (E2M1 values from the magnitude table, E4M3 from the landmark-checked decode)."""
+    """Y = X (value(q) s) for every format against exact rational arithmetic
+    (E2M1 values from the magnitude table, the others from the landmark-checked
+    decode)."""
     rng = np.random.default_rng(2200)
-    for fmt, bits in ((0, 4), (1, 8)):
+    for fmt, bits in ((0, 4), (1, 8), (2, 6), (3, 6)):
         M, K, N, G = 2, 64, 3, 32
-        hi = 16 if fmt == 0 else 256
+        hi = 1 << bits
         codes = rng.integers(0, hi, (K, N))
         if fmt == 1:
             codes[(codes & 0x7F) == 0x7F] = 0x3A   # NaN codes are not inputs
@@ -360,7 +388,7 @@ def pin_float_code_product_bruteforce(orc):
                 for i in range(K):
                     q = int(codes[i, n])
                     val = (Fraction(E2M1_MAGNITUDES[q & 7]) * (-1 if q & 8 else 1)) if fmt == 0 else \
-                        Fraction(orc.float_code_value(q, 1))
+                        Fraction(orc.float_code_value(q, fmt))
                     t = Fraction(float(X[m, i])) * val * Fraction(float(s[n, i // G]))
                     exact += t
                     aabs += abs(t)

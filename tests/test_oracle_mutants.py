@@ -69,6 +69,12 @@ MUTANTS = {
                            "return sign * (e == 0 ? ldexp(1.0 + (double)m / 8.0, -7) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));"),
     "e4m3_mantissa_halved": ("return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7));",
                              "return sign * (e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 16.0, (int)e - 7));"),
+    "fp6_formats_swapped": ("const int mb = fmt == 2 ? 2 : 3, bias = fmt == 2 ? 3 : 1;",
+                            "const int mb = fmt == 2 ? 3 : 2, bias = fmt == 2 ? 1 : 3;"),
+    "fp6_no_subnormals": ("return sign * (e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, (int)e - bias));",
+                          "return sign * (e == 0 ? ldexp(1.0 + frac, -bias) : ldexp(1.0 + frac, (int)e - bias));"),
+    "fp6_sign_bit_wrong": ("const double sign = (q & 0x20u) ? -1.0 : 1.0;",
+                           "const double sign = (q & 0x10u) ? -1.0 : 1.0;"),
     "fp_product_scale_dropped": ("w[i] = float_code_value(column_code(col, i, bits), fmt) * s[n * ngroups + i / G];",
                                  "w[i] = float_code_value(column_code(col, i, bits), fmt);"),
     "sampled_drops_scale": ("            double w = (q - zero_point(z, n, g, ngroups, bits)) * s[n * ngroups + g];",
