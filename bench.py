@@ -250,12 +250,15 @@ def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
 
 
+FP_NAMES = {0: "E2M1", 1: "E4M3", 2: "E3M2", 3: "E2M3"}
+
+
 def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
     """qmm_gemm_fp on the prefill shape (M 2048, K = N = 4096, G 128) with E2M1
-    (fmt 0) or E4M3 (fmt 1) codes: TFLOP/s against the dense fp16 MFMA peak."""
+    (fmt 0), E4M3 (fmt 1) or E3M2 (fmt 2) codes: TFLOP/s against the dense fp16 MFMA peak."""
     w = synthetic.PREFILL
     M, K, N, G = w["M"], w["K"], w["N"], w["G"]
-    bits = 4 if fmt == 0 else 8
+    bits = {0: 4, 1: 8, 2: 6, 3: 6}[fmt]
     g = synthetic.rng(synthetic.seed_for(4, bits, 11 + fmt))
     codes = g.integers(0, 1 << bits, (K, N))
     if fmt == 1:
@@ -268,17 +271,17 @@ def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
         q.gemm_fp(X, wq, s, fmt, G, out=Y)
     ms = timer.region_ms(lambda i: q.gemm_fp(X, wq, s, fmt, G, out=Y), reps) / reps
     tfs = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"workload": f"prefill-gemm {'E2M1' if fmt == 0 else 'E4M3'} codes M{M} K{K} N{N} G{G}",
+    return {"workload": f"prefill-gemm {FP_NAMES[fmt]} codes M{M} K{K} N{N} G{G}",
             "us": round(ms * 1e3, 2), "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
 
 
 def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
     """qmm_gemm_fp at M = 1, 8, 16 on the 7B MLP shape (K 4096, N 11008, G 128)
-    with E2M1 (fmt 0) or E4M3 (fmt 1) codes: weights streamed from HBM
+    with E2M1 (fmt 0), E4M3 (fmt 1) or E3M2 (fmt 2) codes: weights streamed from HBM
     (rotating copies); HBM GB/s of the algorithmic bytes."""
     w = synthetic.DECODE_7B
     K, N, G = w["K"], w["N"], w["G"]
-    bits = 4 if fmt == 0 else 8
+    bits = {0: 4, 1: 8, 2: 6, 3: 6}[fmt]
     g = synthetic.rng(synthetic.seed_for(2, bits, 13 + fmt))
     codes = g.integers(0, 1 << bits, (K, N))
     if fmt == 1:
@@ -287,7 +290,7 @@ def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
     s = torch.from_numpy(synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G))).to("cuda:0")
     bufs = rotating(torch, (wq, s))
     X = torch.from_numpy(synthetic.fp16_normal(g, (16, K))).to("cuda:0")
-    out = {"workload": f"decode {'E2M1' if fmt == 0 else 'E4M3'} codes 7B-MLP K{K} N{N} G{G}"}
+    out = {"workload": f"decode {FP_NAMES[fmt]} codes 7B-MLP K{K} N{N} G{G}"}
     for M in (1, 8, 16):
         x = X[:M].contiguous()
         Y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
@@ -423,7 +426,9 @@ def main():
                  "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
                  "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1),
                  "decode_fp4_e2m1": decode_fp_suite(torch, q, synthetic, timer, reps, 0),
-                 "decode_fp8_e4m3": decode_fp_suite(torch, q, synthetic, timer, reps, 1)}
+                 "decode_fp8_e4m3": decode_fp_suite(torch, q, synthetic, timer, reps, 1),
+                 "prefill_fp6_e3m2": gemm_fp_suite(torch, q, synthetic, timer, reps, 2),
+                 "decode_fp6_e3m2": decode_fp_suite(torch, q, synthetic, timer, reps, 2)}
 
     cpu = None
     if not args.no_cpu:

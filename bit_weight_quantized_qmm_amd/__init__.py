@@ -19,7 +19,7 @@ import torch
 from ._build import LIBRARY
 
 __all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemm", "gemm_fp", "FP4_E2M1",
-           "FP8_E4M3", "gemm_w4a8", "gemm_wka8", "quantize",
+           "FP8_E4M3", "FP6_E3M2", "FP6_E2M3", "gemm_w4a8", "gemm_wka8", "quantize",
            "library_path", "SYMBOLS"]
 
 SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_fp", "qmm_gemm_w4a8", "qmm_gemm_wka8",
@@ -152,12 +152,13 @@ def gemm(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
     return _product(_lib.qmm_gemm, X, wq, s, z, bits, G, out)
 
 
-FP4_E2M1, FP8_E4M3 = 0, 1
-_FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8}
+FP4_E2M1, FP8_E4M3, FP6_E3M2, FP6_E2M3 = 0, 1, 2, 3
+_FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8, FP6_E3M2: 6, FP6_E2M3: 6}
 
 
 def gemm_fp(X, wq, s, fmt: int, G: int, out=None) -> torch.Tensor:
-    """Y [M, N] fp16 = X . (value(q) s) for floating-point codes (FP4_E2M1 or FP8_E4M3)."""
+    """Y [M, N] fp16 = X . (value(q) s) for floating-point codes (FP4_E2M1, FP8_E4M3,
+    FP6_E3M2 or FP6_E2M3)."""
     _need(X, "X", torch.float16)
     M, K = X.shape
     N = s.shape[0]

@@ -119,13 +119,14 @@ qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s,
                        int64_t N, int fmt, int64_t G, qmm_stream stream)
 {
     const char *fn = "qmm_gemm_fp";
-    if (fmt != QMM_FP4_E2M1 && fmt != QMM_FP8_E4M3) return fail(QMM_ERR_INVALID_ARG, "%s: unknown code format", fn);
-    const int bits = fmt == QMM_FP4_E2M1 ? 4 : 8;
+    if (fmt != QMM_FP4_E2M1 && fmt != QMM_FP8_E4M3 && fmt != QMM_FP6_E3M2 && fmt != QMM_FP6_E2M3)
+        return fail(QMM_ERR_INVALID_ARG, "%s: unknown code format", fn);
+    const int bits = fmt == QMM_FP4_E2M1 ? 4 : fmt == QMM_FP8_E4M3 ? 8 : 6;
     qmm_status st = check_shape(fn, M, K, N, bits, G, true);
     if (st != QMM_OK) return st;
     if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
     qmm::GemvArgs a{X, wq, s, nullptr, Y, (int)M, (int)K, (int)N, bits, (int)G};
-    const int f = fmt == QMM_FP4_E2M1 ? 0 : 1;
+    const int f = fmt;   // 0 E2M1, 1 E4M3, 2 E3M2, 3 E2M3
     if (M <= 16) {   // the decode kernels where they take the shape
         const hipError_t e = qmm::launch_gemv_fp(a, f, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e, fn);

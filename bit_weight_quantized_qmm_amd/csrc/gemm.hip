@@ -13,9 +13,10 @@
 // (lanes 16g..16g+15) of every MFMA owns run 4t+g.
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
-// streams; qmm_gemm_fp) keep the codes in order, so X is staged unpermuted.
-// gfx950's packed fp4 / fp8 -> f16 conversions give two codes' exact values
-// per VALU op; one multiply applies s (one rounding).
+// streams, FMT 3 / 4: E3M2 / E2M3 in 6-bit streams; qmm_gemm_fp) keep the
+// codes in order, so X is staged unpermuted.  gfx950's packed fp4 / fp8 -> f16
+// conversions give two codes' exact values per VALU op, the fp6 one a whole
+// run's 32; one multiply applies s (one rounding).
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -181,9 +182,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             half2_t s2;
             s2[0] = as_half(scur[ns]);
             s2[1] = s2[0];
+            uint32_t hf[16];
+            fp_run_to_half2<FMT>(dcur[ns], hf);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const half2_t w = fp_code_pair<FMT>(dcur[ns], j) * s2;   // exact value, one rounding
+                const half2_t w = as_half2(hf[j]) * s2;   // exact value, one rounding
                 bq[ns][j >> 2][2 * (j & 3)] = w[0];
                 bq[ns][j >> 2][2 * (j & 3) + 1] = w[1];
             }
@@ -300,6 +303,8 @@ hipError_t launch_gemm_fp(const GemvArgs &a, int fmt, hipStream_t st)
 {
     if (fmt == 0 && a.bits == 4) return gemm_dispatch<4, 1>(a, st);
     if (fmt == 1 && a.bits == 8) return gemm_dispatch<8, 2>(a, st);
+    if (fmt == 2 && a.bits == 6) return gemm_dispatch<6, 3>(a, st);
+    if (fmt == 3 && a.bits == 6) return gemm_dispatch<6, 4>(a, st);
     return hipErrorInvalidValue;
 }
 

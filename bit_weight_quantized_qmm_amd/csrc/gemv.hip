@@ -231,8 +231,7 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
                 for (int j = 0; j < RPL; ++j) {
                     uint32_t h[16];
                     if constexpr (FMT != 0) {
-#pragma unroll
-                        for (int p = 0; p < 16; ++p) h[p] = as_u32(fp_code_pair<FMT>(d[q][j], p));
+                        fp_run_to_half2<FMT>(d[q][j], h);
                     } else {
                         run_to_half2<BITS>(d[q][j], h);
                     }
@@ -746,8 +745,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                 const uint32_t szv = sz[min((t * 128) / G, ng - 1) * SZW + 16 * j + c];
                 uint32_t h[16];
                 if constexpr (FMT != 0) {
-#pragma unroll
-                    for (int p = 0; p < 16; ++p) h[p] = as_u32(fp_code_pair<FMT>(d[slot], p));
+                    fp_run_to_half2<FMT>(d[slot], h);
                 } else {
                     run_to_half2<BITS>(d[slot], h);
                 }
@@ -1016,7 +1014,7 @@ static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
     return a.z ? gemv_mfma_launch<BITS, true>(a, st) : gemv_mfma_launch<BITS, false>(a, st);
 }
 
-// Floating-point codes (FMT 1: E2M1, 2: E4M3; no zero-point) at M = 1 on the
+// Floating-point codes (FMT 1: E2M1, 2: E4M3, 3: E3M2, 4: E2M3; no zero-point) at M = 1 on the
 // decode kernel and at 2 <= M <= 16 on the MFMA GEMV: hipErrorNotSupported
 // outside their shapes.
 template <int BITS, int FMT>
@@ -1039,6 +1037,8 @@ hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st)
 {
     if (fmt == 0 && a.bits == 4) return gemv_small_fp<4, 1>(a, st);
     if (fmt == 1 && a.bits == 8) return gemv_small_fp<8, 2>(a, st);
+    if (fmt == 2 && a.bits == 6) return gemv_small_fp<6, 3>(a, st);
+    if (fmt == 3 && a.bits == 6) return gemv_small_fp<6, 4>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -119,6 +119,33 @@ __device__ __forceinline__ half2_t fp_code_pair(const uint32_t *d, int j)
     }
 }
 
+// A whole run of floating-point codes as 16 fp16 pairs (pair p = codes 2p and
+// 2p + 1, exact values): per pair for E2M1 / E4M3, and one packed conversion
+// of all 32 codes for the 6-bit formats (FMT 3: E3M2, 4: E2M3), whose source
+// is the run's 6 dwords in stream order.
+template <int FMT, int BITS>
+__device__ __forceinline__ void fp_run_to_half2(const uint32_t (&d)[BITS], uint32_t (&h)[16])
+{
+    if constexpr (FMT == 3 || FMT == 4) {
+        static_assert(BITS == 6, "6-bit float codes");
+        typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+        typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+        typedef _Float16 half32_t __attribute__((ext_vector_type(32)));
+        const u32x6_t src = {d[0], d[1], d[2], d[3], d[4], d[5]};
+        half32_t r;
+        if constexpr (FMT == 3)
+            r = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(src, 1.0f);
+        else
+            r = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(src, 1.0f);
+        const u32x16_t w = __builtin_bit_cast(u32x16_t, r);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) h[p] = w[p];
+    } else {
+#pragma unroll
+        for (int p = 0; p < 16; ++p) h[p] = as_u32(fp_code_pair<FMT>(d, p));
+    }
+}
+
 // fp32 -> fp16 round to nearest even (v_cvt_f16_f32).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return as_u16((_Float16)v); }
 

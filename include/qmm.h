@@ -127,19 +127,21 @@ qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
  * forward implications). */
 enum {
     QMM_FP4_E2M1 = 0,   /* 4-bit stream: sign, 2 exponent bits (bias 1), 1 mantissa bit; 0..6 */
-    QMM_FP8_E4M3 = 1    /* 8-bit stream: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0..448,
+    QMM_FP8_E4M3 = 1,   /* 8-bit stream: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0..448,
                            codes 0x7F / 0xFF (NaN) are not valid weights */
+    QMM_FP6_E3M2 = 2,   /* 6-bit stream: sign, 3 exponent bits (bias 3), 2 mantissa bits; 0..28 */
+    QMM_FP6_E2M3 = 3    /* 6-bit stream: sign, 2 exponent bits (bias 1), 3 mantissa bits; 0..7.5 */
 };
 
 /* Y = X . W with W[k][n] = value(q[k][n]) * s[n][k / G] for floating-point codes
- * (no zero-point), any M >= 1: gfx950's fp4 / fp8 -> f16 conversions give the
+ * (no zero-point), any M >= 1: gfx950's fp4 / fp6 / fp8 -> f16 conversions give the
  * codes' exact values.  At M = 1 with K <= 16384, N <= 65536 the decode kernel runs (fp32
  * dot products of X with the values, s applied per group in fp32); at
  * 2 <= M <= 16 with G % 128 == 0, K <= 8192 the MFMA GEMV (f16 MFMA of X with
  * the values, fp32 accumulation, s applied per 128-row step in fp32);
  * otherwise the qmm_gemm kernel (one rounding multiply by s, then f16 MFMA
  * with fp32 accumulation).  wq is qmm_pack's stream of the code bit
- * patterns at 4 bits (E2M1) or 8 bits (E4M3); X, s, Y, M, K, N, G, stream and
+ * patterns at 4 bits (E2M1), 6 bits (E3M2, E2M3) or 8 bits (E4M3); X, s, Y, M, K, N, G, stream and
  * the errors as for qmm_gemm; an unknown fmt gives QMM_ERR_INVALID_ARG. */
 qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s, qmm_half *Y, int64_t M,
                        int64_t K, int64_t N, int fmt, int64_t G, qmm_stream stream);

@@ -152,7 +152,7 @@ def test_pack_signed_validation(lib):
 
 def test_gemm_fp_validation(lib):
     f = lib.qmm_gemm_fp
-    for fmt in (-1, 2, 7):
+    for fmt in (-1, 4, 7):
         assert f(FAKE, FAKE, FAKE, FAKE, 4, 256, 8, fmt, 64, None) == INVALID
     assert f(None, FAKE, FAKE, FAKE, 4, 256, 8, 0, 64, None) == INVALID
     assert f(FAKE, FAKE, None, FAKE, 4, 256, 8, 1, 64, None) == INVALID

@@ -571,16 +571,25 @@ def test_smallest_quantize(q, orc, bits):
 
 
 # ------------------------------------------------- floating-point codes ---
+FP_FORMATS = [0, 1, 2, 3]   # E2M1, E4M3, E3M2, E2M3
+FP_WIDTH = {0: 4, 1: 8, 2: 6, 3: 6}
+
+
 def fp_codes(fmt, K, N, seed):
     g = synthetic.rng(seed)
-    if fmt == 0:
-        return g.integers(0, 16, (K, N)).astype(np.uint8)
-    q = g.integers(0, 256, (K, N))
-    q[(q & 0x7F) == 0x7F] = 0x30        # NaN patterns are not weights
+    q = g.integers(0, 1 << FP_WIDTH[fmt], (K, N))
+    if fmt == 1:
+        q[(q & 0x7F) == 0x7F] = 0x30        # NaN patterns are not weights
     return q.astype(np.uint8)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+def all_fp_codes(fmt):
+    """Every valid code of a format (E4M3 without its two NaN patterns)."""
+    allq = np.arange(1 << FP_WIDTH[fmt])
+    return allq[(allq & 0x7F) != 0x7F] if fmt == 1 else allq
+
+
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 @pytest.mark.parametrize("M", [1, 5, 130])
 @pytest.mark.parametrize("G", [64, 128])
 def test_gemm_fp_codes(q, orc, fmt, M, G):
@@ -595,7 +604,7 @@ def test_gemm_fp_codes(q, orc, fmt, M, G):
     assert rel_err(Y, ref) <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 @pytest.mark.parametrize("K,N,G", [(32, 7, 32), (1056, 301, 32), (4096, 11008, 128), (8192, 1000, 128),
                                    (16384, 515, 256), (16416, 64, 32)])
 def test_gemm_fp_decode_shapes(q, orc, fmt, K, N, G):
@@ -611,12 +620,12 @@ def test_gemm_fp_decode_shapes(q, orc, fmt, K, N, G):
     assert rel_err(Y, ref) <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
     """M = 1, X one-hot at row i: Y[n] = fp16(value(q[i, n]) s) for every code,
     each in its own column, at a row in the middle of a run and of a group."""
     bits = orc.FP_BITS[fmt]
-    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    allq = all_fp_codes(fmt)
     K, G = 512, 128
     N = len(allq)
     s = synthetic.fp16_uniform(synthetic.rng(450 + fmt), 0.5, 2.0, (N, K // G))
@@ -631,7 +640,7 @@ def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
         assert np.array_equal(Y[0].astype(np.float64), expect.astype(np.float64)), i
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 @pytest.mark.parametrize("M,K,N,G", [(2, 128, 17, 128), (8, 4096, 11008, 128), (16, 8192, 1000, 256),
                                      (3, 1024, 300, 1024), (16, 8320, 40, 128)])
 def test_gemm_fp_batched_shapes(q, orc, fmt, M, K, N, G):
@@ -647,12 +656,12 @@ def test_gemm_fp_batched_shapes(q, orc, fmt, M, K, N, G):
     assert rel_err(Y, ref) <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 def test_gemm_fp_batched_reads_every_code_exactly(q, orc, fmt):
     """M = 16, row m of X one-hot at a different row i_m (even and odd code
     positions, run and group boundaries): Y[m][n] = fp16(value(q[i_m][n]) s)."""
     bits = orc.FP_BITS[fmt]
-    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    allq = all_fp_codes(fmt)
     K, G = 512, 128
     N = len(allq)
     rows = [0, 1, 13, 31, 32, 45, 127, 128, 255, 256, 300, 383, 400, 450, 500, 511]
@@ -669,12 +678,12 @@ def test_gemm_fp_batched_reads_every_code_exactly(q, orc, fmt):
         assert np.array_equal(Y[m].astype(np.float64), expect.astype(np.float64)), (m, i)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", FP_FORMATS)
 def test_gemm_fp_decodes_every_code_exactly(q, orc, fmt):
     """One-hot rows of X read single weights back: Y = fp16(value(q) s) bit for bit
     for every code (both signs, subnormals, the largest values)."""
     bits = orc.FP_BITS[fmt]
-    allq = np.arange(16) if fmt == 0 else np.array([v for v in range(256) if (v & 0x7F) != 0x7F])
+    allq = all_fp_codes(fmt)
     K, G = 256, 128
     N = 64
     codes = np.zeros((K, N), dtype=np.uint8)
