@@ -641,7 +641,8 @@ def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", FP_FORMATS)
-@pytest.mark.parametrize("M,K,N,G", [(2, 128, 17, 128), (8, 4096, 11008, 128), (16, 8192, 1000, 256),
+@pytest.mark.parametrize("M,K,N,G", [(2, 128, 17, 128), (8, 4096, 11008, 128), (16, 4096, 11008, 128),
+                                     (16, 8192, 1000, 256),
                                      (3, 1024, 300, 1024), (16, 8320, 40, 128)])
 def test_gemm_fp_batched_shapes(q, orc, fmt, M, K, N, G):
     """2 <= M <= 16 float-code products: one 128-row step with a ragged tile,
@@ -676,6 +677,24 @@ def test_gemm_fp_batched_reads_every_code_exactly(q, orc, fmt):
         vals = np.array([orc.float_code_value(int(v), fmt) for v in codes[i]])
         expect = (vals * s[:, i // G].astype(np.float64)).astype(np.float16)
         assert np.array_equal(Y[m].astype(np.float64), expect.astype(np.float64)), (m, i)
+
+
+@pytest.mark.parametrize("fmt", FP_FORMATS)
+def test_gemm_fp_prefill_workload(q, orc, fmt):
+    """The prefill shape (M 2048, K = N = 4096, G 128) in the launch the bench
+    times; the oracle checks 16 rows of Y (first, last, tile edges, random) in
+    full, since rows of Y are independent."""
+    w = synthetic.PREFILL
+    M, K, N, G = w["M"], w["K"], w["N"], w["G"]
+    bits = orc.FP_BITS[fmt]
+    codes = fp_codes(fmt, K, N, 520 + fmt)
+    c = synthetic.make_case(M, K, N, bits, G, 530 + fmt, s_range=w["s_range"])
+    wq = q.pack(dev(codes), bits)
+    Y = q.gemm_fp(dev(c["X"]), wq, dev(c["s"]), fmt, G)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, 1024, 2046, 2047],
+                                     synthetic.rng(540 + fmt).integers(0, M, 8)]))
+    ref = orc.qmm_fp(c["X"][rows], orc.pack(codes, bits), c["s"], fmt, G)
+    assert rel_err(Y[torch.as_tensor(rows, device=Y.device)], ref) <= TOL
 
 
 @pytest.mark.parametrize("fmt", FP_FORMATS)
