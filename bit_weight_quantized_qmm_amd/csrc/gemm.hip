@@ -8,8 +8,8 @@
 // run's half-slot order and scaled by 2^-p, so both MFMA operands are plain
 // 16-byte fragments.
 //
-// Workgroup tile 128 (M) x 256 (N), 4 waves side by side in N, wave tile
-// 128 x 64 = 8 x 4 MFMA tiles.  K advances 128 rows per step: lane group g
+// Workgroup tile 128 (M) x 256 (N), 8 waves side by side in N, wave tile
+// 128 x 32 = 8 x 2 MFMA tiles.  K advances 128 rows per step: lane group g
 // (lanes 16g..16g+15) of every MFMA owns run 4t+g.
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
@@ -70,15 +70,19 @@ __device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &
     nt = in_band / rows;
 }
 
-// Workgroup tile 128 (M) x 256 (N): 4 waves side by side in N, each 128 x 64
-// = 8 x 4 MFMA tiles, so every weight run is dequantised by exactly one lane.
+// Workgroup tile 128 (M) x 256 (N): 8 waves side by side in N, each 128 x 32
+// = 8 x 2 MFMA tiles, so every weight run is dequantised by exactly one lane.
+// Two waves per SIMD: one wave's dequantisation and X staging run while the
+// other's MFMAs issue (the wave's accumulators, B fragments and one K slice of
+// A fragments fit in half the register file).
 template <int BITS, bool PGZ, int FMT>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
                                                    int ntiles)
 {
     using P = RunPlan<BITS>;
+    constexpr int NS = 2;   // 16-column subtiles per wave: 8 waves x 32 columns
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GEMM_BM * GEMM_ROWB];
 
     int mt, nt;
@@ -95,28 +99,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     const int mrows = min(GEMM_BM, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
     // Weights, scales, zero-points of this wave's 64 columns.
-    const int wn0 = n0 + wave * 64;
-    const int wcols = max(0, min(64, N - wn0));
+    const int wn0 = n0 + wave * 32;
+    const int wcols = max(0, min(32, N - wn0));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)min(wn0, N) * ng, (uint32_t)(wcols * ng * 2));
     const __amdgpu_buffer_rsrc_t zr =
         make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
 
-    // X staging: 128 rows x 4 runs of 64 bytes per step, two (row, run) pieces per thread.
-    auto load_x = [&](int tt, uint32_t (&raw)[2][16]) {
+    // X staging: 128 rows x 4 runs of 64 bytes per step, one (row, run) piece per thread.
+    auto load_x = [&](int tt, uint32_t (&raw)[1][16]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int it = tid + 256 * i;
+        for (int i = 0; i < 1; ++i) {
+            const int it = tid + 512 * i;
             const int row = it >> 2, gg = it & 3;
             const int run = 4 * tt + gg;
             const uint32_t off = (run < R) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
             load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
         }
     };
-    auto store_x = [&](int buf, const uint32_t (&raw)[2][16]) {
+    auto store_x = [&](int buf, const uint32_t (&raw)[1][16]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int it = tid + 256 * i;
+        for (int i = 0; i < 1; ++i) {
+            const int it = tid + 512 * i;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
             if constexpr (FMT == 0) {
@@ -137,10 +141,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             }
         }
     };
-    auto load_w = [&](int tt, uint32_t (&d)[4][BITS], uint16_t (&sv)[4], uint16_t (&zv)[4]) {
+    auto load_w = [&](int tt, uint32_t (&d)[NS][BITS], uint16_t (&sv)[NS], uint16_t (&zv)[NS]) {
         const int run = 4 * tt + g;
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
             const int col = ns * 16 + c;
             const uint32_t off = (run < R) ? (uint32_t)col * col_bytes + (uint32_t)run * run_bytes : GEMM_OOB;
             load_dwords<LOAD_STREAM>(wr, off, d[ns], BITS);
@@ -150,15 +154,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
         }
     };
 
-    float4_t acc[8][4];
+    float4_t acc[8][NS];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NS; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t xraw[2][16];
-    uint32_t dcur[4][BITS], dnext[4][BITS];
-    uint16_t scur[4], snext[4], zcur[4], znext[4];
+    uint32_t xraw[1][16];
+    uint32_t dcur[NS][BITS], dnext[NS][BITS];
+    uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
     load_x(0, xraw);
     load_w(0, dcur, scur, zcur);
     store_x(0, xraw);
@@ -175,9 +179,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
         load_x(tt + 1, xraw);
         load_w(tt + 1, dnext, snext, znext);
         // dequantise this step's 4 runs (one per N subtile) into B fragments
-        half8_t bq[4][4];
+        half8_t bq[NS][4];
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
           if constexpr (FMT != 0) {
             half2_t s2;
             s2[0] = as_half(scur[ns]);
@@ -225,27 +229,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
           }
         }
         const uint8_t *abase = abase0 + cur * (GEMM_BM * GEMM_ROWB);
-        // All 32 A fragments of the step stay in registers while the MFMAs walk
-        // the four column tiles in turn, so dequantising tile ns + 1 overlaps the
-        // MFMAs of tile ns.
-        half8_t a[4][8];
+        // per 32-row K slice u: the 8 A fragments of the wave's 128 rows, then
+        // the slice's MFMAs over both column subtiles
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
+            half8_t a[8];
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) a[u][ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
+            for (int ms = 0; ms < 8; ++ms) a[ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
                 for (int ms = 0; ms < 8; ++ms)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u][ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
+        }
         // the X permutation waits for this step's prefetch: keep it after the MFMAs
         __builtin_amdgcn_sched_barrier(0);
         store_x(cur ^ 1, xraw);
         __syncthreads();
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
             for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
             scur[ns] = snext[ns];
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
             const int col = wn0 + ns * 16 + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -272,7 +274,7 @@ template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
     const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + GEMM_BN - 1) / GEMM_BN;
-    const dim3 block(256), grid((unsigned)(mtiles * ntiles));
+    const dim3 block(512), grid((unsigned)(mtiles * ntiles));
     if (FMT == 0 && a.z)
         hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K,
                            a.N, a.G, mtiles, ntiles);
