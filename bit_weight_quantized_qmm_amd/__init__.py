@@ -159,10 +159,12 @@ _FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8, FP6_E3M2: 6, FP6_E2M3: 6}
 def gemm_fp(X, wq, s, fmt: int, G: int, out=None) -> torch.Tensor:
     """Y [M, N] fp16 = X . (value(q) s) for floating-point codes (FP4_E2M1, FP8_E4M3,
     FP6_E3M2 or FP6_E2M3)."""
+    if fmt not in _FP_BITS:
+        raise ValueError(f"unknown float code format {fmt}: expected one of {sorted(_FP_BITS)}")
     _need(X, "X", torch.float16)
     M, K = X.shape
     N = s.shape[0]
-    _need(wq, "wq", torch.int32, (N, K * _FP_BITS.get(fmt, 0) // 32), X.device)
+    _need(wq, "wq", torch.int32, (N, K * _FP_BITS[fmt] // 32), X.device)
     _need(s, "s", torch.float16, (N, K // G), X.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)

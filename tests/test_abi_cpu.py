@@ -150,6 +150,17 @@ def test_pack_signed_validation(lib):
     assert f(FAKE, FAKE, 250, 8, 4, None) == INVALID
 
 
+def test_binding_rejects_unknown_float_format():
+    """The binding names an unknown code format before looking at any tensor."""
+    import torch
+    import bit_weight_quantized_qmm_amd as q
+    X = torch.zeros((1, 64), dtype=torch.float16)
+    for fmt in (-1, 4):
+        with pytest.raises(ValueError, match="unknown float code format"):
+            q.gemm_fp(X, X, X, fmt, 32)
+    assert (q.FP4_E2M1, q.FP8_E4M3, q.FP6_E3M2, q.FP6_E2M3) == (0, 1, 2, 3)
+
+
 def test_gemm_fp_validation(lib):
     f = lib.qmm_gemm_fp
     for fmt in (-1, 4, 7):
