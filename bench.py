@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--no-suite", action="store_true", help="skip the batched-decode and W4A8 timings")
+    ap.add_argument("--no-suite", action="store_true", help="skip the suite (batched decode, int8 activations, quantiser, float codes)")
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
@@ -341,7 +341,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported here "
-              f"(the product shards by output column, see the design notes).", file=sys.stderr)
+              f"(the product shards by output column: one process per GPU, each with its own slice of N).", file=sys.stderr)
         return 2
     import torch
     import bit_weight_quantized_qmm_amd as q
