@@ -110,6 +110,6 @@ def test_mutant_is_caught(name, tmp_path):
     proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     line = [l for l in proc.stdout.splitlines() if l.startswith("FAILED_PINS")]
     if proc.returncode != 0 and not line:
-        return  # the mutant crashed the checker outright: caught
+        return  # the mutant crashed the pin run outright: caught
     failed = line[0].split(" ", 1)[1] if line and " " in line[0] else ""
     assert failed.strip(), f"mutant {name} passed every pin"
