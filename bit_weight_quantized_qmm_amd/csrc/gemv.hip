@@ -76,7 +76,9 @@ constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every resource w
 // go out before the weight loads, so the staging overlaps the weight stream.
 // Lane l owns runs l, l+64, ... (RPL of them); per run 16 v_dot2_f32_f16 give
 // a = sum x'(1024 + q 2^p), and y += s_g * (a - bias).  A DPP reduction
-// finishes each column.
+// finishes each column.  Floating-point codes (FMT != 0): X is staged in code
+// order without bias sums, the run's pairs come from the packed fp4 / fp6 /
+// fp8 conversions (exact values), and y += s_g * a.
 // ---------------------------------------------------------------------------
 template <int CTRL, int ROWM, int BANKM, bool BC>
 __device__ __forceinline__ float dpp_add(float v)
