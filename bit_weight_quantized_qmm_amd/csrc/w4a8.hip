@@ -392,8 +392,10 @@ static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
     const int mtiles = (a.M + 15) / 16;
     if (mtiles > 65535) return hipErrorNotSupported;
     const int tiles = (a.N + 15) / 16;
-    int cus = 256, dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
     const int per_m = std::max(1, cus / mtiles);
     const int tpw = std::min(8, std::max(1, (tiles + per_m - 1) / per_m));   // one batch of tiles per workgroup
     const dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)mtiles);
