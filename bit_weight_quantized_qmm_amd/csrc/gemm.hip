@@ -9,8 +9,10 @@
 // 16-byte fragments.
 //
 // Workgroup tile 128 (M) x 256 (N), 8 waves side by side in N, wave tile
-// 128 x 32 = 8 x 2 MFMA tiles.  K advances 128 rows per step: lane group g
-// (lanes 16g..16g+15) of every MFMA owns run 4t+g.
+// 128 x 32 = 8 x 2 MFMA tiles; products too small to give every CU a
+// workgroup that way take 128-, 64- or 32-column tiles (8, 4 or 2 waves of
+// 16 columns).  K advances 128 rows per step: lane group g (lanes
+// 16g..16g+15) of every MFMA owns run 4t+g.
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
 // streams, FMT 3 / 4: E3M2 / E2M3 in 6-bit streams; qmm_gemm_fp) keep the
@@ -48,7 +50,7 @@ __device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs
     }
 }
 
-constexpr int GEMM_BM = 128, GEMM_BN = 256;
+constexpr int GEMM_BM = 128;
 constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
 constexpr int GEMM_GROUP_M = 4;          // M tiles per band of the tile order
 constexpr uint32_t GEMM_OOB = 0x80000000u;
@@ -70,24 +72,26 @@ __device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &
     nt = in_band / rows;
 }
 
-// Workgroup tile 128 (M) x 256 (N): 8 waves side by side in N, each 128 x 32
-// = 8 x 2 MFMA tiles, so every weight run is dequantised by exactly one lane.
-// Two waves per SIMD: one wave's dequantisation and X staging run while the
-// other's MFMAs issue (the wave's accumulators, B fragments and one K slice of
-// A fragments fit in half the register file).
-template <int BITS, bool PGZ, int FMT>
-__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+// Workgroup tile 128 (M) x 16 NS WV (N): WV waves side by side in N, each
+// 128 x 16 NS = 8 x NS MFMA tiles, so every weight run is dequantised by
+// exactly one lane.  With 8 waves, two share each SIMD: one wave's
+// dequantisation and X staging run while the other's MFMAs issue (the wave's
+// accumulators, B fragments and one K slice of A fragments fit in half the
+// register file).
+template <int BITS, bool PGZ, int FMT, int WV, int NS>
+__global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
                                                    int ntiles)
 {
     using P = RunPlan<BITS>;
-    constexpr int NS = 2;   // 16-column subtiles per wave: 8 waves x 32 columns
+    constexpr int BN = 16 * NS * WV;   // workgroup columns: WV waves of 16 NS columns
+    constexpr int XP = 512 / (64 * WV);   // (row, run) pieces of the X step per thread
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GEMM_BM * GEMM_ROWB];
 
     int mt, nt;
     gemm_tile(mtiles, ntiles, mt, nt);
-    const int m0 = mt * GEMM_BM, n0 = nt * GEMM_BN;
+    const int m0 = mt * GEMM_BM, n0 = nt * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
@@ -99,28 +103,28 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
     const int mrows = min(GEMM_BM, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
     // Weights, scales, zero-points of this wave's 64 columns.
-    const int wn0 = n0 + wave * 32;
-    const int wcols = max(0, min(32, N - wn0));
+    const int wn0 = n0 + wave * 16 * NS;
+    const int wcols = max(0, min(16 * NS, N - wn0));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)min(wn0, N) * ng, (uint32_t)(wcols * ng * 2));
     const __amdgpu_buffer_rsrc_t zr =
         make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
 
     // X staging: 128 rows x 4 runs of 64 bytes per step, one (row, run) piece per thread.
-    auto load_x = [&](int tt, uint32_t (&raw)[1][16]) {
+    auto load_x = [&](int tt, uint32_t (&raw)[XP][16]) {
 #pragma unroll
-        for (int i = 0; i < 1; ++i) {
-            const int it = tid + 512 * i;
+        for (int i = 0; i < XP; ++i) {
+            const int it = tid + 64 * WV * i;
             const int row = it >> 2, gg = it & 3;
             const int run = 4 * tt + gg;
             const uint32_t off = (run < R) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
             load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
         }
     };
-    auto store_x = [&](int buf, const uint32_t (&raw)[1][16]) {
+    auto store_x = [&](int buf, const uint32_t (&raw)[XP][16]) {
 #pragma unroll
-        for (int i = 0; i < 1; ++i) {
-            const int it = tid + 512 * i;
+        for (int i = 0; i < XP; ++i) {
+            const int it = tid + 64 * WV * i;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
             if constexpr (FMT == 0) {
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t xraw[1][16];
+    uint32_t xraw[XP][16];
     uint32_t dcur[NS][BITS], dnext[NS][BITS];
     uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
     load_x(0, xraw);
@@ -270,18 +274,43 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
     }
 }
 
+template <int BITS, int FMT, int WV, int NS>
+static hipError_t gemm_go(const GemvArgs &a, hipStream_t st)
+{
+    constexpr int BN = 16 * NS * WV;
+    const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + BN - 1) / BN;
+    const dim3 block(64 * WV), grid((unsigned)(mtiles * ntiles));
+    if (FMT == 0 && a.z)
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+                           a.K, a.N, a.G, mtiles, ntiles);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+                           a.K, a.N, a.G, mtiles, ntiles);
+    return hipGetLastError();
+}
+
+static int gemm_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        cus = (hipGetDevice(&dev) == hipSuccess &&
+               hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+    }
+    return cus;
+}
+
+// The widest column tile whose grid still has a workgroup per CU: 256 columns
+// (8 waves of 32) for large M x N, then 128, 64 and 32 for smaller products,
+// where every workgroup otherwise runs the whole K loop with CUs idle.
 template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
-    const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + GEMM_BN - 1) / GEMM_BN;
-    const dim3 block(512), grid((unsigned)(mtiles * ntiles));
-    if (FMT == 0 && a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K,
-                           a.N, a.G, mtiles, ntiles);
-    else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M, a.K,
-                           a.N, a.G, mtiles, ntiles);
-    return hipGetLastError();
+    const long long mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, cus = gemm_cus();
+    if (mtiles * ((a.N + 255) / 256) >= cus) return gemm_go<BITS, FMT, 8, 2>(a, st);
+    if (mtiles * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1>(a, st);
+    if (mtiles * ((a.N + 63) / 64) >= cus) return gemm_go<BITS, FMT, 4, 1>(a, st);
+    return gemm_go<BITS, FMT, 2, 1>(a, st);
 }
 
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)
