@@ -10,8 +10,8 @@
 //
 // Workgroup tile 128 (M) x 256 (N), 8 waves side by side in N, wave tile
 // 128 x 32 = 8 x 2 MFMA tiles; products too small to give every CU a
-// workgroup that way take 128-, 64- or 32-column tiles (8, 4 or 2 waves of
-// 16 columns).  K advances 128 rows per step: lane group g (lanes
+// workgroup that way take 128 x 128, 64 x 128 or 64 x 64 tiles (8, 8 or 4
+// waves of 16 columns).  K advances 128 rows per step: lane group g (lanes
 // 16g..16g+15) of every MFMA owns run 4t+g.
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
@@ -50,7 +50,6 @@ __device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs
     }
 }
 
-constexpr int GEMM_BM = 128;
 constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
 constexpr int GEMM_GROUP_M = 4;          // M tiles per band of the tile order
 constexpr uint32_t GEMM_OOB = 0x80000000u;
@@ -72,13 +71,13 @@ __device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &
     nt = in_band / rows;
 }
 
-// Workgroup tile 128 (M) x 16 NS WV (N): WV waves side by side in N, each
-// 128 x 16 NS = 8 x NS MFMA tiles, so every weight run is dequantised by
+// Workgroup tile BM (M) x 16 NS WV (N): WV waves side by side in N, each
+// BM x 16 NS = BM/16 x NS MFMA tiles, so every weight run is dequantised by
 // exactly one lane.  With 8 waves, two share each SIMD: one wave's
 // dequantisation and X staging run while the other's MFMAs issue (the wave's
 // accumulators, B fragments and one K slice of A fragments fit in half the
 // register file).
-template <int BITS, bool PGZ, int FMT, int WV, int NS>
+template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM>
 __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
@@ -86,12 +85,13 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 {
     using P = RunPlan<BITS>;
     constexpr int BN = 16 * NS * WV;   // workgroup columns: WV waves of 16 NS columns
-    constexpr int XP = 512 / (64 * WV);   // (row, run) pieces of the X step per thread
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][GEMM_BM * GEMM_ROWB];
+    constexpr int MS = BM / 16;                               // 16-row MFMA tiles per wave
+    constexpr int XP = (BM * 4 + 64 * WV - 1) / (64 * WV);   // (row, run) pieces of the X step per thread
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * GEMM_ROWB];
 
     int mt, nt;
     gemm_tile(mtiles, ntiles, mt, nt);
-    const int m0 = mt * GEMM_BM, n0 = nt * BN;
+    const int m0 = mt * BM, n0 = nt * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
@@ -100,9 +100,9 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const float zdef = (float)(1u << (BITS - 1));
 
     // X: rows m0.. of the whole K range (rows past M and runs past K read zeros).
-    const int mrows = min(GEMM_BM, M - m0);
+    const int mrows = min(BM, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
-    // Weights, scales, zero-points of this wave's 64 columns.
+    // Weights, scales, zero-points of this wave's 16 NS columns.
     const int wn0 = n0 + wave * 16 * NS;
     const int wcols = max(0, min(16 * NS, N - wn0));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
@@ -110,14 +110,14 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const __amdgpu_buffer_rsrc_t zr =
         make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
 
-    // X staging: 128 rows x 4 runs of 64 bytes per step, one (row, run) piece per thread.
+    // X staging: BM rows x 4 runs of 64 bytes per step, XP (row, run) pieces per thread.
     auto load_x = [&](int tt, uint32_t (&raw)[XP][16]) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int it = tid + 64 * WV * i;
             const int row = it >> 2, gg = it & 3;
             const int run = 4 * tt + gg;
-            const uint32_t off = (run < R) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
+            const uint32_t off = (run < R && it < BM * 4) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
             load_dwords<LOAD_DEFAULT>(xr, off, raw[i], 16);
         }
     };
@@ -125,6 +125,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int it = tid + 64 * WV * i;
+            if (it >= BM * 4) break;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
             if constexpr (FMT == 0) {
@@ -158,9 +159,9 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
         }
     };
 
-    float4_t acc[8][NS];
+    float4_t acc[MS][NS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -232,18 +233,18 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             }
           }
         }
-        const uint8_t *abase = abase0 + cur * (GEMM_BM * GEMM_ROWB);
-        // per 32-row K slice u: the 8 A fragments of the wave's 128 rows, then
+        const uint8_t *abase = abase0 + cur * (BM * GEMM_ROWB);
+        // per 32-row K slice u: the MS A fragments of the wave's BM rows, then
         // the slice's MFMAs over both column subtiles
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            half8_t a[8];
+            half8_t a[MS];
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) a[ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
+            for (int ms = 0; ms < MS; ++ms) a[ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-                for (int ms = 0; ms < 8; ++ms)
+                for (int ms = 0; ms < MS; ++ms)
                     acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
         }
         // the X permutation waits for this step's prefetch: keep it after the MFMAs
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 
     // epilogue: lane (g, c) of MFMA tile (ms, ns) holds rows 4g..4g+3, column c.
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
+    for (int ms = 0; ms < MS; ++ms) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
             const int col = wn0 + ns * 16 + c;
@@ -274,17 +275,17 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     }
 }
 
-template <int BITS, int FMT, int WV, int NS>
+template <int BITS, int FMT, int WV, int NS, int BM>
 static hipError_t gemm_go(const GemvArgs &a, hipStream_t st)
 {
     constexpr int BN = 16 * NS * WV;
-    const int mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, ntiles = (a.N + BN - 1) / BN;
+    const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
     const dim3 block(64 * WV), grid((unsigned)(mtiles * ntiles));
     if (FMT == 0 && a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     return hipGetLastError();
 }
@@ -300,17 +301,20 @@ static int gemm_cus()
     return cus;
 }
 
-// The widest column tile whose grid still has a workgroup per CU: 256 columns
-// (8 waves of 32) for large M x N, then 128, 64 and 32 for smaller products,
-// where every workgroup otherwise runs the whole K loop with CUs idle.
+// Tile choice: the first of 128 x 256 (8 waves of 32 columns), 128 x 128 and
+// 64 x 128 (8 waves of 16), 64 x 64 (4 waves of 16) whose grid gives every CU
+// a workgroup, else 64 x 64.  Each workgroup runs the whole K loop, so a grid
+// smaller than the CU count leaves the time of one workgroup's loop for a
+// fraction of the work; 8-wave tiles keep two waves per SIMD.
 template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
-    const long long mtiles = (a.M + GEMM_BM - 1) / GEMM_BM, cus = gemm_cus();
-    if (mtiles * ((a.N + 255) / 256) >= cus) return gemm_go<BITS, FMT, 8, 2>(a, st);
-    if (mtiles * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1>(a, st);
-    if (mtiles * ((a.N + 63) / 64) >= cus) return gemm_go<BITS, FMT, 4, 1>(a, st);
-    return gemm_go<BITS, FMT, 2, 1>(a, st);
+    const long long cus = gemm_cus();
+    const long long m128 = (a.M + 127) / 128, m64 = (a.M + 63) / 64;
+    if (m128 * ((a.N + 255) / 256) >= cus) return gemm_go<BITS, FMT, 8, 2, 128>(a, st);
+    if (m128 * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1, 128>(a, st);
+    if (m64 * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1, 64>(a, st);
+    return gemm_go<BITS, FMT, 4, 1, 64>(a, st);
 }
 
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)

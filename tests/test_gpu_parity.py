@@ -254,12 +254,13 @@ def test_batched_70b_workload(q, orc, bits):
 
 
 @pytest.mark.parametrize("M,K,N,bits", [(2048, 256, 4096, 4), (1024, 512, 4056, 3), (512, 512, 4096, 5),
-                                         (512, 256, 4000, 8), (130, 512, 300, 4), (17, 1024, 2000, 6)])
-def test_gemm_column_tile_widths(q, orc, M, K, N, bits):
-    """Shapes that select each column tile of the GEMM on a 256-CU part: 256
-    columns (M 2048), 128 (M 1024), 64 (M 512) and 32 (small products), with
-    ragged last tiles; every width computes each output with the same MFMA
-    sequence, so all are checked against the oracle in full."""
+                                         (500, 256, 4000, 8), (256, 512, 4096, 4), (130, 512, 300, 4),
+                                         (17, 1024, 2000, 6)])
+def test_gemm_tile_shapes(q, orc, M, K, N, bits):
+    """Shapes that select each GEMM tile on a 256-CU part: 128 x 256 (M 2048),
+    128 x 128 (M 1024), 64 x 128 (M 500, 512), 64 x 64 (M 256 and the small
+    products), with ragged M and N edges; every tile computes each output with
+    the same MFMA sequence, so all are checked against the oracle in full."""
     c = synthetic.make_case(M, K, N, bits, 128, 560 + M + N + bits, per_group_z=(bits == 5))
     Y = run_product(q, q.gemm, c)
     ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, 128)
