@@ -172,7 +172,7 @@ class Oracle:
         return f(q, fmt)
 
     def qmm_fp(self, X, stream, s, fmt: int, G: int, N: int | None = None) -> np.ndarray:
-        """float64 Y = X . (value(q) * s) for floating-point codes (0: E2M1, 1: E4M3)."""
+        """float64 Y = X . (value(q) * s) for floating-point codes (0: E2M1, 1: E4M3, 2: E3M2, 3: E2M3)."""
         X64 = self._f64(X)
         M, K = X64.shape
         if N is None:
