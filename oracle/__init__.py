@@ -163,7 +163,7 @@ class Oracle:
         return A, Y
 
 
-    FP_BITS = {0: 4, 1: 8, 2: 6, 3: 6}   # format -> code width: E2M1, E4M3, E3M2, E2M3
+    FP_BITS = {0: 4, 1: 8, 2: 6, 3: 6, 4: 3, 5: 5, 6: 7}   # E2M1, E4M3, E3M2, E2M3, E1M1, E2M2, E3M3
 
     def float_code_value(self, q: int, fmt: int) -> float:
         f = self.lib.qmm_oracle_float_code_value
@@ -172,7 +172,8 @@ class Oracle:
         return f(q, fmt)
 
     def qmm_fp(self, X, stream, s, fmt: int, G: int, N: int | None = None) -> np.ndarray:
-        """float64 Y = X . (value(q) * s) for floating-point codes (0: E2M1, 1: E4M3, 2: E3M2, 3: E2M3)."""
+        """float64 Y = X . (value(q) * s) for floating-point codes (0: E2M1, 1: E4M3, 2: E3M2, 3: E2M3,
+        4: E1M1, 5: E2M2, 6: E3M3)."""
         X64 = self._f64(X)
         M, K = X64.shape
         if N is None:

@@ -47,7 +47,11 @@
  * mantissa pattern is NaN, no infinities), and at 6 bits the two OCP FP6
  * formats, E3M2 (3 exponent bits with bias 3, 2 mantissa bits) and E2M3
  * (2 exponent bits with bias 1, 3 mantissa bits), both with subnormals at
- * exponent 0 and every code finite.  w = value(q) * s, no zero-point.
+ * exponent 0 and every code finite.  The 3-, 5- and 7-bit widths follow the
+ * rule those three formats share (of the k - 1 bits after the sign, the
+ * extra one goes to the exponent): E1M1 (bias 0), E2M2 (bias 1) and E3M3
+ * (bias 3), subnormals at exponent 0, every code finite.  w = value(q) * s,
+ * no zero-point.
  *
  * The quantiser (qmm_oracle_quantize) follows eq. (1) of the same section,
  * q = clip(round(w / s) + z, 0, 2^k - 1), with s and z chosen per (column,
@@ -302,8 +306,9 @@ int qmm_oracle_quantize(const double *W, int64_t K, int64_t N, int bits, int64_t
 }
 
 /* Value of a floating-point code: fmt 0 = E2M1 (4-bit), fmt 1 = E4M3 (8-bit),
- * fmt 2 = E3M2 and fmt 3 = E2M3 (6-bit), from the sign / exponent / mantissa
- * fields as defined above. */
+ * fmt 2 = E3M2 and fmt 3 = E2M3 (6-bit), fmt 4 = E1M1 (3-bit), fmt 5 = E2M2
+ * (5-bit), fmt 6 = E3M3 (7-bit), from the sign / exponent / mantissa fields
+ * as defined above. */
 static double float_code_value(unsigned q, int fmt)
 {
     if (fmt == 0) {
@@ -318,6 +323,13 @@ static double float_code_value(unsigned q, int fmt)
         const double frac = ldexp((double)m, -mb);
         return sign * (e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, (int)e - bias));
     }
+    if (fmt >= 4 && fmt <= 6) {   /* E1M1, E2M2, E3M3: k = 3, 5, 7 */
+        const int eb = fmt - 3, mbits = fmt - 3, k = 1 + eb + mbits, bias = (1 << (eb - 1)) - 1;
+        const double sign = ((q >> (k - 1)) & 1u) ? -1.0 : 1.0;
+        const unsigned e = (q >> mbits) & ((1u << eb) - 1u), m = q & ((1u << mbits) - 1u);
+        const double frac = ldexp((double)m, -mbits);
+        return sign * (e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, (int)e - bias));
+    }
     const double sign = (q & 0x80u) ? -1.0 : 1.0;
     const unsigned e = (q >> 3) & 15u, m = q & 7u;
     if (e == 15 && m == 7) return NAN;
@@ -328,11 +340,12 @@ double qmm_oracle_float_code_value(unsigned q, int fmt) { return float_code_valu
 
 /* Y = X . W with W[i][n] = value(q[i][n]) * s[n][i / G] for floating-point codes
  * (fmt 0: E2M1 in 4-bit streams, fmt 1: E4M3 in 8-bit streams, fmt 2 / 3:
- * E3M2 / E2M3 in 6-bit streams), fp64. */
+ * E3M2 / E2M3 in 6-bit streams, fmt 4 / 5 / 6: E1M1 / E2M2 / E3M3 in 3-, 5-
+ * and 7-bit streams), fp64. */
 int qmm_oracle_qmm_fp(const double *X, const uint8_t *stream, const double *s, int64_t M, int64_t K, int64_t N,
                       int fmt, int64_t G, double *Y)
 {
-    const int bits = fmt == 0 ? 4 : fmt == 1 ? 8 : (fmt == 2 || fmt == 3) ? 6 : 0;
+    const int bits = fmt == 0 ? 4 : fmt == 1 ? 8 : (fmt == 2 || fmt == 3) ? 6 : (fmt >= 4 && fmt <= 6) ? 2 * fmt - 5 : 0;
     if (!shape_ok(K, N, bits) || !groups_ok(K, G) || M < 0) return -1;
     if ((M > 0 && N > 0) && (!Y || (K > 0 && (!X || !stream || !s)))) return -1;
     const int64_t colbytes = K * bits / 8, ngroups = K / G;

@@ -339,14 +339,17 @@ def pin_e4m3_landmarks(orc):
     assert mags[1] - mags[0] == 2.0 ** -9 and mags[9] - mags[8] == 2.0 ** -9
 
 
-def _fp6_landmarks(v, one, min_normal, min_sub, max_code, max_val, per_binade):
+def _float_landmarks(v, one, min_normal, min_sub, max_code, max_val, per_binade):
+    """Checks for a format whose codes (len(v) of them) carry the sign in the top
+    bit, every code finite, subnormals at exponent 0."""
+    half = len(v) // 2
     assert v[one] == 1.0 and v[per_binade] == min_normal and v[1] == min_sub and v[max_code] == max_val
     assert not any(np.isnan(x) or np.isinf(x) for x in v)     # every code finite
-    for q in range(32):
-        assert v[q + 0x20] == -v[q] and np.signbit(v[q + 0x20])
-    mags = v[:32]
+    for q in range(half):
+        assert v[q + half] == -v[q] and np.signbit(v[q + half])
+    mags = v[:half]
     assert all(b > a for a, b in zip(mags, mags[1:]))
-    for q in range(0, 32, per_binade):   # equal steps inside each binade
+    for q in range(0, half, per_binade):   # equal steps inside each binade
         assert len({mags[q + j + 1] - mags[q + j] for j in range(per_binade - 1)}) == 1, q
     # subnormals continue the first normal binade's step
     assert mags[1] - mags[0] == min_sub and mags[per_binade + 1] - mags[per_binade] == min_sub
@@ -356,14 +359,34 @@ def pin_e3m2_landmarks(orc):
     """E3M2 (6-bit, bias 3): 1.0 = 0x0C, 0.25 = 0x04 (smallest normal),
     0.0625 = 0x01 (smallest subnormal), 28 = 0x1F (largest), bit 5 the sign,
     4 codes per binade, every code finite."""
-    _fp6_landmarks([orc.float_code_value(q, 2) for q in range(64)], 0x0C, 0.25, 0.0625, 0x1F, 28.0, 4)
+    _float_landmarks([orc.float_code_value(q, 2) for q in range(64)], 0x0C, 0.25, 0.0625, 0x1F, 28.0, 4)
 
 
 def pin_e2m3_landmarks(orc):
     """E2M3 (6-bit, bias 1): 1.0 = 0x08 (smallest normal), 0.125 = 0x01
     (smallest subnormal), 7.5 = 0x1F (largest), bit 5 the sign, 8 codes per
     binade, every code finite."""
-    _fp6_landmarks([orc.float_code_value(q, 3) for q in range(64)], 0x08, 1.0, 0.125, 0x1F, 7.5, 8)
+    _float_landmarks([orc.float_code_value(q, 3) for q in range(64)], 0x08, 1.0, 0.125, 0x1F, 7.5, 8)
+
+
+def pin_e1m1_values(orc):
+    """E1M1 (3-bit, bias 0): codes 0..3 are 0, 1, 2, 3; bit 2 the sign."""
+    v = [orc.float_code_value(q, 4) for q in range(8)]
+    assert v[:4] == [0.0, 1.0, 2.0, 3.0]
+    _float_landmarks(v, 0x1, 2.0, 1.0, 0x3, 3.0, 2)
+
+
+def pin_e2m2_landmarks(orc):
+    """E2M2 (5-bit, bias 1): 0.25 = 0x01 (smallest subnormal), 1.0 = 0x04
+    (smallest normal), 7 = 0x0F (largest), bit 4 the sign, 4 codes per binade."""
+    _float_landmarks([orc.float_code_value(q, 5) for q in range(32)], 0x04, 1.0, 0.25, 0x0F, 7.0, 4)
+
+
+def pin_e3m3_landmarks(orc):
+    """E3M3 (7-bit, bias 3): 2^-5 = 0x01 (smallest subnormal), 0.25 = 0x08
+    (smallest normal), 1.0 = 0x18, 30 = 0x3F (largest), bit 6 the sign, 8 codes
+    per binade."""
+    _float_landmarks([orc.float_code_value(q, 6) for q in range(128)], 0x18, 0.25, 2.0 ** -5, 0x3F, 30.0, 8)
 
 
 def pin_float_code_product_bruteforce(orc):
@@ -371,7 +394,7 @@ def pin_float_code_product_bruteforce(orc):
     (E2M1 values from the magnitude table, the others from the landmark-checked
     decode)."""
     rng = np.random.default_rng(2200)
-    for fmt, bits in ((0, 4), (1, 8), (2, 6), (3, 6)):
+    for fmt, bits in ((0, 4), (1, 8), (2, 6), (3, 6), (4, 3), (5, 5), (6, 7)):
         M, K, N, G = 2, 64, 3, 32
         hi = 1 << bits
         codes = rng.integers(0, hi, (K, N))

@@ -75,6 +75,10 @@ MUTANTS = {
                           "return sign * (e == 0 ? ldexp(1.0 + frac, -bias) : ldexp(1.0 + frac, (int)e - bias));"),
     "fp6_sign_bit_wrong": ("const double sign = (q & 0x20u) ? -1.0 : 1.0;",
                            "const double sign = (q & 0x10u) ? -1.0 : 1.0;"),
+    "fp357_bias_off_by_one": ("const int eb = fmt - 3, mbits = fmt - 3, k = 1 + eb + mbits, bias = (1 << (eb - 1)) - 1;",
+                              "const int eb = fmt - 3, mbits = fmt - 3, k = 1 + eb + mbits, bias = (1 << (eb - 1));"),
+    "fp357_sign_bit_wrong": ("const double sign = ((q >> (k - 1)) & 1u) ? -1.0 : 1.0;",
+                             "const double sign = ((q >> (k - 2)) & 1u) ? -1.0 : 1.0;"),
     "fp_product_scale_dropped": ("w[i] = float_code_value(column_code(col, i, bits), fmt) * s[n * ngroups + i / G];",
                                  "w[i] = float_code_value(column_code(col, i, bits), fmt);"),
     "sampled_drops_scale": ("            double w = (q - zero_point(z, n, g, ngroups, bits)) * s[n * ngroups + g];",
