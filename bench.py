@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-suite", action="store_true", help="skip the suite (batched decode, int8 activations, quantiser, float codes)")
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--only", default=None,
+                    help="run one leg and print its JSON (for profiling): decode, gemm, batched, w4a8, w8a8, "
+                         "quantize, fp, lut, probes")
+    ap.add_argument("--bits", type=int, default=None, help="with --only: restrict to one code width")
+    ap.add_argument("--M", type=int, default=None, help="with --only batched: restrict to one M")
     return ap.parse_args()
 
 
@@ -87,6 +92,7 @@ class Timer:
 
     def __init__(self, torch):
         self.torch = torch
+        self.quick = False   # --only runs (under a profiler): a few regions instead of 50
 
     def region_ms(self, launch, count):
         torch = self.torch
@@ -100,6 +106,29 @@ class Timer:
         ev1.record()
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1)
+
+    def median_us(self, launch, per_region=10, regions=50):
+        """Median and mean per-launch time (us) over `regions` regions of
+        `per_region` back-to-back launches each (the median of 50 of the
+        pages' protocol, taken over short regions because a single launch is
+        too short to bracket with events without inflating it)."""
+        torch = self.torch
+        if self.quick:
+            regions = min(regions, 2)
+        vals = []
+        for r in range(regions):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for i in range(per_region):
+                launch(r * per_region + i)
+            ev1.record()
+            torch.cuda.synchronize()
+            vals.append(ev0.elapsed_time(ev1) * 1e3 / per_region)
+        vals.sort()
+        return float(np.median(vals)), float(np.mean(vals))
 
 
 def decode_setup(torch, q, synthetic, bits):
@@ -144,9 +173,23 @@ def traffic_for(kernel_key):
     return e.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synthetic, budget_s=12.0):
-    """The oracle as it stands, timed on this host: the same decode step
-    (k = 3, 4, 6) repeated until about budget_s seconds have passed."""
+    """The oracle as it stands, timed on this host.  `value`: the same decode
+    step as the GPU's (k = 3, 4, 6) repeated until about budget_s seconds have
+    passed.  `configs`: one timing each of the tiny case, one 70B MLP-up
+    batched-decode row, the W4A8 product and a bounded row sample of the
+    prefill product (scaled to the full shape), each a few seconds at most."""
     import oracle
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     orc = oracle.default()
@@ -165,9 +208,49 @@ def cpu_baseline(synthetic, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    del cases
+    configs = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    t = synthetic.TINY
+    c = synthetic.make_case(1, t["K"], t["N"], 4, t["G"], synthetic.seed_for(1, 4), s_range=t["s_range"])
+    st = orc.pack(c["codes"], 4)
+    n = 200
+    sec = timed(lambda: [orc.qmm(c["X"], st, c["s"], None, 4, t["G"]) for _ in range(n)]) / n
+    configs["tiny"] = {"workload": t["name"], "ms": round(sec * 1e3, 4), "packed_GBs": round(st.size / sec / 1e9, 4)}
+    b = synthetic.BATCHED_70B
+    c = synthetic.make_case(1, b["K"], b["N"], 1, b["G"], synthetic.seed_for(3, 1), per_group_z=True, s_range=b["s_range"])
+    st = orc.pack(c["codes"], 1)
+    del c["codes"]
+    sec = timed(lambda: orc.qmm(c["X"], st, c["s"], c["z"], 1, b["G"]))
+    configs["batched_70b_k1_M1"] = {"workload": "batched-decode 70B-MLP-up M1 K8192 N28672 k1 G128 per-group z",
+                                    "ms": round(sec * 1e3, 2), "packed_GBs": round(st.size / sec / 1e9, 4)}
+    del st
+    a = synthetic.W4A8_8B
+    c = synthetic.make_w4a8_case(a["M"], a["K"], a["N"], a["G"], synthetic.seed_for(5, 4), s_range=a["s_range"])
+    st = orc.pack(c["codes"], 4)
+    del c["codes"]
+    sec = timed(lambda: orc.w4a8(c["Xq"], c["sx"], st, c["s"], None, a["G"]))
+    configs["w4a8_8b"] = {"workload": a["name"], "ms": round(sec * 1e3, 2), "packed_GBs": round(st.size / sec / 1e9, 4),
+                          "GOPs": round(2.0 * a["M"] * a["K"] * a["N"] / sec / 1e9, 3)}
+    del st
+    p = synthetic.PREFILL
+    c = synthetic.make_case(p["M"], p["K"], p["N"], 4, p["G"], synthetic.seed_for(4, 4), s_range=p["s_range"])
+    st = orc.pack(c["codes"], 4)
+    rows = 16
+    sec = timed(lambda: orc.qmm(c["X"][:rows], st, c["s"], None, 4, p["G"]))
+    full = sec * p["M"] / rows
+    configs["prefill"] = {"workload": p["name"], "sample": f"{rows} of {p['M']} rows, time scaled to all rows",
+                          "s_full_estimate": round(full, 2), "GFLOPs": round(2.0 * p["M"] * p["K"] * p["N"] / full / 1e9, 3)}
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{reps} x the full decode step (k=3,4,6; M=1 K=4096 N=11008): bit-serial unpack, "
-                      f"fp64 dequant and fp64 dot products, {dt:.1f} s wall"}
+                      f"fp64 dequant and fp64 dot products, {dt:.1f} s wall",
+            "configs": configs}
 
 
 def rotating(torch, tensors):
@@ -178,13 +261,15 @@ def rotating(torch, tensors):
     return [tuple(t.clone() for t in tensors) for _ in range(copies)]
 
 
-def batched_suite(torch, q, synthetic, timer, reps):
+def batched_suite(torch, q, synthetic, timer, reps, only_bits=None, only_m=None):
     """70B MLP-up batched decode (K 8192, N 28672, G 128, per-group z) at M = 1, 8, 16
     for k = 1, 2, 5, 7, 8: us per launch and HBM GB/s of the algorithmic bytes."""
     w = synthetic.BATCHED_70B
     K, N, G = w["K"], w["N"], w["G"]
     out = {}
     for bits in w["bits"]:
+        if only_bits is not None and bits != only_bits:
+            continue
         c = synthetic.make_case(max(w["Ms"]), K, N, bits, G, synthetic.seed_for(3, bits), per_group_z=True,
                                 s_range=w["s_range"])
         wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), bits)
@@ -193,6 +278,8 @@ def batched_suite(torch, q, synthetic, timer, reps):
         X = torch.from_numpy(c["X"]).to("cuda:0")
         row = {}
         for M in w["Ms"]:
+            if only_m is not None and M != only_m:
+                continue
             x = X[:M].contiguous()
             y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
             state = {"i": 0}
@@ -250,7 +337,8 @@ def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
 
 
-FP_NAMES = {0: "E2M1", 1: "E4M3", 2: "E3M2", 3: "E2M3"}
+FP_NAMES = {0: "E2M1", 1: "E4M3", 2: "E3M2", 3: "E2M3", 4: "E1M1", 5: "E2M2", 6: "E3M3"}
+FP_BITS = {0: 4, 1: 8, 2: 6, 3: 6, 4: 3, 5: 5, 6: 7}
 
 
 def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
@@ -258,7 +346,7 @@ def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
     (fmt 0), E4M3 (fmt 1) or E3M2 (fmt 2) codes: TFLOP/s against the dense fp16 MFMA peak."""
     w = synthetic.PREFILL
     M, K, N, G = w["M"], w["K"], w["N"], w["G"]
-    bits = {0: 4, 1: 8, 2: 6, 3: 6}[fmt]
+    bits = FP_BITS[fmt]
     g = synthetic.rng(synthetic.seed_for(4, bits, 11 + fmt))
     codes = g.integers(0, 1 << bits, (K, N))
     if fmt == 1:
@@ -267,11 +355,22 @@ def gemm_fp_suite(torch, q, synthetic, timer, reps, fmt):
     s = torch.from_numpy(synthetic.fp16_uniform(g, 0.002, 0.02, (N, K // G))).to("cuda:0")
     X = torch.from_numpy(synthetic.fp16_normal(g, (M, K))).to("cuda:0")
     Y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    bufs = rotating(torch, (X, wq, s))
+    state = {"i": 0}
+
+    def launch(i):
+        b = bufs[state["i"] % len(bufs)]
+        state["i"] += 1
+        q.gemm_fp(b[0], b[1], b[2], fmt, G, out=Y)
+
     for _ in range(3):
-        q.gemm_fp(X, wq, s, fmt, G, out=Y)
-    ms = timer.region_ms(lambda i: q.gemm_fp(X, wq, s, fmt, G, out=Y), reps) / reps
+        launch(0)
+    ms = timer.region_ms(launch, reps) / reps
     tfs = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    del bufs
+    torch.cuda.empty_cache()
     return {"workload": f"prefill-gemm {FP_NAMES[fmt]} codes M{M} K{K} N{N} G{G}",
+            "cache": "cold (rotating X, Wq, s copies > 1 GiB)",
             "us": round(ms * 1e3, 2), "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
 
 
@@ -281,7 +380,7 @@ def decode_fp_suite(torch, q, synthetic, timer, reps, fmt):
     (rotating copies); HBM GB/s of the algorithmic bytes."""
     w = synthetic.DECODE_7B
     K, N, G = w["K"], w["N"], w["G"]
-    bits = {0: 4, 1: 8, 2: 6, 3: 6}[fmt]
+    bits = FP_BITS[fmt]
     g = synthetic.rng(synthetic.seed_for(2, bits, 13 + fmt))
     codes = g.integers(0, 1 << bits, (K, N))
     if fmt == 1:
@@ -337,6 +436,107 @@ def quantize_suite(torch, q, synthetic, timer, reps):
             "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def probes_leg(torch, q, timer):
+    """Measured ceilings on this GPU: a plain streaming read of the decode
+    weights' sizes (and of 1 GiB) from HBM, and back-to-back f16 MFMAs on
+    register operands.  Reported beside the datasheet peaks, never instead."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    big = torch.empty(3 << 28, dtype=torch.int32, device="cuda:0").fill_(7)   # 3 GiB, rotated through
+    total = big.numel() * 4
+    out = {"read": {}, "mfma": {}}
+    sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda:0")
+    for name, nbytes in (("7B_k3_16.9MB", 16908288), ("7B_k4_22.5MB", 22544384), ("7B_k6_33.8MB", 33816576),
+                         ("1GiB", 1 << 30)):
+        best = None
+        for wpc in (1, 2, 4, 8):
+            grid = cus * wpc
+            nslices = max(2, total // nbytes - 1)
+            state = {"i": 0}
+
+            def launch(i, nbytes=nbytes, grid=grid, nslices=nslices, state=state):
+                off = (state["i"] % nslices) * nbytes
+                state["i"] += 1
+                q.probe_read(big.view(torch.uint8)[off:off + nbytes], grid, sink)
+
+            launch(0)
+            per = 4 if nbytes >= (1 << 30) else 10
+            med, mean = timer.median_us(launch, per_region=per, regions=10 if nbytes >= (1 << 30) else 30)
+            r = {"workgroups_per_cu": wpc, "us_median": round(med, 3), "GBs": round(nbytes / med / 1e3, 1)}
+            if best is None or r["GBs"] > best["GBs"]:
+                best = r
+        best["frac_of_datasheet"] = round(best["GBs"] / HBM_PEAK_GBS, 4)
+        out["read"][name] = best
+    del big
+    torch.cuda.empty_cache()
+    msink = torch.empty(cus * 2 * 512, dtype=torch.float32, device="cuda:0")
+    for shape, name in ((0, "f16_16x16x32"), (1, "f16_32x32x16")):
+        best = None
+        for wpc in (1, 2):
+            grid = cus * wpc
+            iters = 4096 // wpc
+            flops = q.probe_mfma(iters, grid, shape, msink)
+            med, mean = timer.median_us(lambda i: q.probe_mfma(iters, grid, shape, msink), per_region=3, regions=10)
+            tfs = flops / (med * 1e-6) / 1e12
+            r = {"workgroups_per_cu": wpc, "us_median": round(med, 2), "TFLOPs": round(tfs, 1)}
+            if best is None or r["TFLOPs"] > best["TFLOPs"]:
+                best = r
+        best["frac_of_datasheet"] = round(best["TFLOPs"] / FP16_MFMA_PEAK_TFS, 4)
+        out["mfma"][name] = best
+    return out
+
+
+def blas_context(torch, timer):
+    """The library fp16 GEMM (torch.matmul -> hipBLASLt) on the prefill shape
+    with dense fp16 weights: context for the quantised GEMM, not part of the path."""
+    M, K, N = 2048, 4096, 4096
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    A = torch.randn((M, K), device="cuda:0", dtype=torch.float16, generator=g)
+    B = torch.randn((K, N), device="cuda:0", dtype=torch.float16, generator=g)
+    C = torch.empty((M, N), device="cuda:0", dtype=torch.float16)
+    for _ in range(3):
+        torch.matmul(A, B, out=C)
+    med, mean = timer.median_us(lambda i: torch.matmul(A, B, out=C), per_region=5, regions=20)
+    tfs = 2.0 * M * N * K / (med * 1e-6) / 1e12
+    return {"workload": "torch.matmul fp16 M2048 K4096 N4096 (dense weights, warm caches)", "us_median": round(med, 2),
+            "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
+
+
+def gemm_leg(torch, q, synthetic, timer, reps):
+    """The prefill product (M 2048, K = N = 4096, k 4, G 128) on the MFMA path.
+    Cold: every launch reads its own copy of X, Wq and s out of a rotating set
+    above 1 GiB (nothing is found in the 256 MB Infinity Cache); hot: the same
+    inputs every launch, labelled as such."""
+    w = synthetic.PREFILL
+    c = synthetic.make_case(w["M"], w["K"], w["N"], 4, w["G"], synthetic.seed_for(4, 4), s_range=w["s_range"])
+    X = torch.from_numpy(c["X"]).to("cuda:0")
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
+    s = torch.from_numpy(c["s"]).to("cuda:0")
+    Y = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda:0")
+    bufs = rotating(torch, (X, wq, s))
+    state = {"i": 0}
+
+    def cold(i):
+        b = bufs[state["i"] % len(bufs)]
+        state["i"] += 1
+        q.gemm(b[0], b[1], b[2], None, 4, w["G"], out=Y)
+
+    for _ in range(3):
+        cold(0)
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    gms = timer.region_ms(cold, reps) / reps
+    med, mean = timer.median_us(cold, per_region=5, regions=50)
+    hmed, hmean = timer.median_us(lambda i: q.gemm(X, wq, s, None, 4, w["G"], out=Y), per_region=5, regions=20)
+    tfs = flops / (gms * 1e-3) / 1e12
+    del bufs
+    torch.cuda.empty_cache()
+    return {"workload": w["name"], "cache": "cold (rotating X, Wq, s copies > 1 GiB)",
+            "us_per_launch": round(gms * 1e3, 2), "us_median_of_50": round(med, 2), "TFLOPs": round(tfs, 1),
+            "hot_cache": {"us_median": round(hmed, 2), "TFLOPs": round(flops / (hmed * 1e-6) / 1e12, 1)},
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": traffic_for("gemm_k4"),
+                         "kernel": "qmm_gemm M=2048 k=4 (gemm_kernel)", "flops_per_launch": flops}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -351,7 +551,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    print(f"bench: setting up decode workload", file=sys.stderr, flush=True)
+    timer = Timer(torch)
 
     if args.copy_probe:
         a = torch.empty(1 << 28, dtype=torch.int32, device="cuda:0").fill_(1)
@@ -362,8 +562,12 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copies": 3}))
         return 0
 
+    reps = max(10, args.steps // 2)
+    if args.only is not None:
+        return run_only(args, torch, q, synthetic, timer, reps)
+
+    print(f"bench: setting up decode workload", file=sys.stderr, flush=True)
     decs = [decode_setup(torch, q, synthetic, bits) for bits in synthetic.DECODE_7B["bits"]]
-    timer = Timer(torch)
     for _ in range(args.warmup):
         for d in decs:
             decode_launch(q, d)
@@ -376,13 +580,16 @@ def main():
     wq_step = sum(d["wq_bytes"] for d in decs)
     value = wq_step / (ms_per_step * 1e-3) / 1e9
 
-    # each kernel on its own: mean launch duration over the same number of launches
+    # each kernel on its own: mean launch duration over the same number of
+    # launches, and the median over 50 short regions
     per_bits, mean_ms = {}, {}
     for d in decs:
         ms = timer.region_ms(lambda i, d=d: decode_launch(q, d), args.steps) / args.steps
+        med, _ = timer.median_us(lambda i, d=d: decode_launch(q, d), per_region=10, regions=50)
         mean_ms[d["bits"]] = ms
         per_bits[str(d["bits"])] = {
             "us_per_launch": round(ms * 1e3, 3),
+            "us_median_of_50": round(med, 3),
             "packed_GBs": round(d["wq_bytes"] / (ms * 1e-3) / 1e9, 1),
             "algorithmic_GBs": round(d["alg_bytes"] / (ms * 1e-3) / 1e9, 1),
             "packed_frac_of_peak": round(d["wq_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -397,38 +604,22 @@ def main():
     del decs
     torch.cuda.empty_cache()
 
-    # prefill product on the MFMA path
+    print("bench: measured ceilings (stream read, MFMA) and the library fp16 GEMM", file=sys.stderr, flush=True)
+    probes = probes_leg(torch, q, timer)
+    probes["library_fp16_gemm"] = blas_context(torch, timer)
+    for k, r in per_bits.items():
+        name = {"3": "7B_k3_16.9MB", "4": "7B_k4_22.5MB", "6": "7B_k6_33.8MB"}[k]
+        r["frac_of_probe_read"] = round(r["packed_GBs"] / probes["read"][name]["GBs"], 4)
+
     print("bench: timing the M=2048 prefill product", file=sys.stderr, flush=True)
-    w = synthetic.PREFILL
-    c = synthetic.make_case(w["M"], w["K"], w["N"], 4, w["G"], synthetic.seed_for(4, 4), s_range=w["s_range"])
-    X = torch.from_numpy(c["X"]).to("cuda:0")
-    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
-    s = torch.from_numpy(c["s"]).to("cuda:0")
-    Y = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda:0")
-    for _ in range(3):
-        q.gemm(X, wq, s, None, 4, w["G"], out=Y)
-    nrep = max(10, args.steps // 2)
-    gms = timer.region_ms(lambda i: q.gemm(X, wq, s, None, 4, w["G"], out=Y), nrep) / nrep
-    flops = 2.0 * w["M"] * w["N"] * w["K"]
-    tfs = flops / (gms * 1e-3) / 1e12
-    gemm = {"workload": w["name"], "us_per_launch": round(gms * 1e3, 2), "TFLOPs": round(tfs, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": traffic_for("gemm_k4")}}
+    gemm = gemm_leg(torch, q, synthetic, timer, reps)
+    mfma_probe = max(v["TFLOPs"] for v in probes["mfma"].values())
+    gemm["frac_of_probe_mfma"] = round(gemm["TFLOPs"] / mfma_probe, 4)
 
     suite = None
     if not args.no_suite:
         print("bench: timing the batched-decode and int8-activation workloads", file=sys.stderr, flush=True)
-        reps = max(10, args.steps // 2)
-        suite = {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
-                 "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
-                 "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
-                 "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps),
-                 "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
-                 "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1),
-                 "decode_fp4_e2m1": decode_fp_suite(torch, q, synthetic, timer, reps, 0),
-                 "decode_fp8_e4m3": decode_fp_suite(torch, q, synthetic, timer, reps, 1),
-                 "prefill_fp6_e3m2": gemm_fp_suite(torch, q, synthetic, timer, reps, 2),
-                 "decode_fp6_e3m2": decode_fp_suite(torch, q, synthetic, timer, reps, 2)}
+        suite = run_suite(torch, q, synthetic, timer, reps)
 
     cpu = None
     if not args.no_cpu:
@@ -446,11 +637,66 @@ def main():
         "roofline": roofline,
         "per_bits": per_bits,
         "gemm_m2048": gemm,
+        "probes": probes,
         "suite": suite,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_suite(torch, q, synthetic, timer, reps):
+    return {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
+            "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
+            "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
+            "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps),
+            "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
+            "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1),
+            "prefill_fp6_e3m2": gemm_fp_suite(torch, q, synthetic, timer, reps, 2),
+            "decode_fp4_e2m1": decode_fp_suite(torch, q, synthetic, timer, reps, 0),
+            "decode_fp8_e4m3": decode_fp_suite(torch, q, synthetic, timer, reps, 1),
+            "decode_fp6_e3m2": decode_fp_suite(torch, q, synthetic, timer, reps, 2),
+            "prefill_fp3_e1m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 4),
+            "prefill_fp5_e2m2": gemm_fp_suite(torch, q, synthetic, timer, reps, 5),
+            "prefill_fp7_e3m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 6),
+            "decode_fp3_e1m1": decode_fp_suite(torch, q, synthetic, timer, reps, 4),
+            "decode_fp5_e2m2": decode_fp_suite(torch, q, synthetic, timer, reps, 5),
+            "decode_fp7_e3m3": decode_fp_suite(torch, q, synthetic, timer, reps, 6)}
+
+
+def run_only(args, torch, q, synthetic, timer, reps):
+    """One leg alone (for rocprofv3 runs): few launches, its JSON on stdout."""
+    name = args.only
+    timer.quick = True
+    print(f"bench: --only {name}", file=sys.stderr, flush=True)
+    if name == "decode":
+        out = {}
+        for bits in synthetic.DECODE_7B["bits"]:
+            if args.bits is not None and bits != args.bits:
+                continue
+            d = decode_setup(torch, q, synthetic, bits)
+            ms = timer.region_ms(lambda i, d=d: decode_launch(q, d), reps) / reps
+            out[f"k{bits}"] = {"us_per_launch": round(ms * 1e3, 3)}
+            del d
+            torch.cuda.empty_cache()
+    elif name == "gemm":
+        out = gemm_leg(torch, q, synthetic, timer, reps)
+    elif name == "batched":
+        out = batched_suite(torch, q, synthetic, timer, reps, only_bits=args.bits, only_m=args.M)
+    elif name in ("w4a8", "w8a8"):
+        out = w4a8_suite(torch, q, synthetic, timer, reps, bits=4 if name == "w4a8" else 8)
+    elif name == "quantize":
+        out = quantize_suite(torch, q, synthetic, timer, reps)
+    elif name == "fp":
+        out = {f"prefill_{k}": gemm_fp_suite(torch, q, synthetic, timer, reps, k) for k in FP_NAMES}
+    elif name == "probes":
+        out = probes_leg(torch, q, timer)
+        out["library_fp16_gemm"] = blas_context(torch, timer)
+    else:
+        print(f"unknown leg {name}", file=sys.stderr)
+        return 2
+    print(json.dumps({"only": name, "result": out}), flush=True)
     return 0
 
 

@@ -18,12 +18,13 @@ import torch
 
 from ._build import LIBRARY
 
-__all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemm", "gemm_fp", "FP4_E2M1",
-           "FP8_E4M3", "FP6_E3M2", "FP6_E2M3", "gemm_w4a8", "gemm_wka8", "quantize",
-           "library_path", "SYMBOLS"]
+__all__ = ["QmmError", "packed_bytes", "pack", "pack_signed", "unpack", "gemv", "gemv_grouped", "gemv_lut", "gemm", "gemm_fp", "FP4_E2M1",
+           "FP8_E4M3", "FP6_E3M2", "FP6_E2M3", "FP3_E1M1", "FP5_E2M2", "FP7_E3M3", "gemm_w4a8", "gemm_wka8", "quantize",
+           "probe_read", "probe_mfma", "library_path", "SYMBOLS"]
 
-SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemm", "qmm_gemm_fp", "qmm_gemm_w4a8", "qmm_gemm_wka8",
-           "qmm_quantize", "qmm_status_string", "qmm_last_error")
+SYMBOLS = ("qmm_packed_bytes", "qmm_pack", "qmm_pack_signed", "qmm_unpack", "qmm_gemv", "qmm_gemv_grouped", "qmm_gemv_lut", "qmm_gemm", "qmm_gemm_fp", "qmm_gemm_w4a8", "qmm_gemm_wka8",
+           "qmm_quantize", "qmm_status_string", "qmm_last_error", "qmm_last_hip_error", "qmm_probe_read",
+           "qmm_probe_mfma")
 
 
 class QmmError(RuntimeError):
@@ -44,12 +45,17 @@ def _load():
         "qmm_unpack": ([P, P, I64, I64, INT, P], INT),
         "qmm_gemv": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_gemv_lut": ([P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
+        "qmm_gemv_grouped": ([P, INT, I64, I64, P], INT),
         "qmm_gemm_fp": ([P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_gemm_w4a8": ([P, P, P, P, P, P, P, I64, I64, I64, I64, P], INT),
         "qmm_gemm_wka8": ([P, P, P, P, P, P, P, I64, I64, I64, INT, I64, P], INT),
         "qmm_quantize": ([P, P, P, P, I64, I64, INT, I64, P], INT),
         "qmm_status_string": ([INT], ctypes.c_char_p),
         "qmm_last_error": ([], ctypes.c_char_p),
+        "qmm_last_hip_error": ([], ctypes.c_char_p),
+        "qmm_probe_read": ([P, ctypes.c_uint64, P, INT, P], INT),
+        "qmm_probe_mfma": ([P, INT, INT, INT, P], INT),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -147,18 +153,54 @@ def gemv(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
     return _product(_lib.qmm_gemv, X, wq, s, z, bits, G, out)
 
 
+class _Problem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("s", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("N", ctypes.c_int64), ("bits", ctypes.c_int)]
+
+
+def gemv_grouped(problems, G: int, outs=None):
+    """Several M = 1 products in one launch.  problems: sequence of (X [1, K], wq, s, z or None,
+    bits) sharing K; returns the list of Y [1, N] (or fills outs)."""
+    problems = list(problems)
+    if not problems:
+        raise ValueError("no problems")
+    K = problems[0][0].shape[1]
+    arr = (_Problem * len(problems))()
+    res = []
+    for i, (X, wq, s, z, bits) in enumerate(problems):
+        _need(X, "X", torch.float16, (1, K))
+        N = s.shape[0]
+        _need(wq, "wq", torch.int32, (N, K * bits // 32), X.device)
+        _need(s, "s", torch.float16, (N, K // G), X.device)
+        if z is not None:
+            _need(z, "z", torch.float16, (N, K // G), X.device)
+        Y = outs[i] if outs is not None else torch.empty((1, N), dtype=torch.float16, device=X.device)
+        _need(Y, "out", torch.float16, (1, N), X.device)
+        arr[i] = _Problem(X.data_ptr(), wq.data_ptr(), s.data_ptr(), 0 if z is None else z.data_ptr(), Y.data_ptr(),
+                          N, bits)
+        res.append(Y)
+    _check(_lib.qmm_gemv_grouped(ctypes.cast(arr, ctypes.c_void_p), len(problems), K, G,
+                                 _stream(problems[0][0].device)))
+    return res
+
+
+def gemv_lut(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
+    """Y [1, N] fp16 = X [1, K] fp16 . dequant(wq) for 1-bit codes by table lookup (K <= 8192)."""
+    return _product(_lib.qmm_gemv_lut, X, wq, s, z, bits, G, out)
+
+
 def gemm(X, wq, s, z, bits: int, G: int, out=None) -> torch.Tensor:
     """Y [M, N] fp16 = X [M, K] fp16 . dequant(wq); any M (f16 MFMA path)."""
     return _product(_lib.qmm_gemm, X, wq, s, z, bits, G, out)
 
 
-FP4_E2M1, FP8_E4M3, FP6_E3M2, FP6_E2M3 = 0, 1, 2, 3
-_FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8, FP6_E3M2: 6, FP6_E2M3: 6}
+FP4_E2M1, FP8_E4M3, FP6_E3M2, FP6_E2M3, FP3_E1M1, FP5_E2M2, FP7_E3M3 = 0, 1, 2, 3, 4, 5, 6
+_FP_BITS = {FP4_E2M1: 4, FP8_E4M3: 8, FP6_E3M2: 6, FP6_E2M3: 6, FP3_E1M1: 3, FP5_E2M2: 5, FP7_E3M3: 7}
 
 
 def gemm_fp(X, wq, s, fmt: int, G: int, out=None) -> torch.Tensor:
     """Y [M, N] fp16 = X . (value(q) s) for floating-point codes (FP4_E2M1, FP8_E4M3,
-    FP6_E3M2 or FP6_E2M3)."""
+    FP6_E3M2, FP6_E2M3, FP3_E1M1, FP5_E2M2 or FP7_E3M3)."""
     if fmt not in _FP_BITS:
         raise ValueError(f"unknown float code format {fmt}: expected one of {sorted(_FP_BITS)}")
     _need(X, "X", torch.float16)
@@ -221,3 +263,29 @@ def quantize(W, bits: int, G: int, codes=None, s=None, z=None):
     _need(z, "z", torch.float16, (N, K // G), W.device)
     _check(_lib.qmm_quantize(_ptr(W), _ptr(codes), _ptr(s), _ptr(z), K, N, bits, G, _stream(W.device)))
     return codes, s, z
+
+
+def probe_read(buf: torch.Tensor, grid: int, sink: torch.Tensor | None = None) -> None:
+    """Measurement hook: one streaming read of the whole of buf (any dtype, contiguous,
+    byte size a multiple of 16) by `grid` workgroups; computes nothing of the product."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, None, buf.device)
+    if sink.numel() < grid * 256:
+        raise ValueError("sink needs grid * 256 elements")
+    _check(_lib.qmm_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), grid, _stream(buf.device)))
+
+
+def probe_mfma(iters: int, grid: int, shape: int = 0, sink: torch.Tensor | None = None,
+               device: str = "cuda:0") -> int:
+    """Measurement hook: back-to-back f16 MFMAs (shape 0: 16x16x32, 1: 32x32x16) on register
+    operands in `grid` workgroups of 8 waves; returns the flops enqueued."""
+    if sink is None:
+        sink = torch.empty(grid * 512, dtype=torch.float32, device=device)
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < grid * 512:
+        raise ValueError("sink needs grid * 512 elements")
+    _check(_lib.qmm_probe_mfma(_ptr(sink), iters, grid, shape, _stream(sink.device)))
+    return grid * 8 * iters * 8 * 16384

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libqmm.so")
-SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "w4a8.hip", "quantize.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "w4a8.hip", "quantize.hip", "probe.hip", "lut.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -109,6 +109,40 @@ qmm_status qmm_gemv(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
     return product("qmm_gemv", true, X, wq, s, z, Y, M, K, N, bits, G, stream);
 }
 
+qmm_status qmm_gemv_grouped(const qmm_gemv_problem *probs, int count, int64_t K, int64_t G, qmm_stream stream)
+{
+    const char *fn = "qmm_gemv_grouped";
+    if (!probs) return fail(QMM_ERR_INVALID_ARG, "%s: null problem array", fn);
+    if (count < 1 || count > qmm::QMM_GROUP_MAX) return fail(QMM_ERR_INVALID_ARG, "%s: count must be in 1..16", fn);
+    qmm::GroupArgs ga{};
+    ga.count = count;
+    ga.K = (int)K;
+    ga.G = (int)G;
+    for (int p = 0; p < count; ++p) {
+        const qmm_gemv_problem &q = probs[p];
+        qmm_status st = check_shape(fn, 1, K, q.N, q.bits, G, true);
+        if (st != QMM_OK) return st;
+        if (!q.X || !q.wq || !q.s || !q.Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer in a problem", fn);
+        if (K > 16384 || (K / 32) * q.N * 4 * (int64_t)q.bits >= (int64_t(1) << 31) - 1)
+            return fail(QMM_ERR_UNSUPPORTED, "%s: K <= 16384 and a problem's weights below 2 GiB are supported", fn);
+        ga.p[p] = qmm::GroupProblem{q.X, q.wq, q.s, q.z, q.Y, (int)q.N, q.bits};
+    }
+    return hip_status(qmm::launch_gemv_grouped(ga, (hipStream_t)stream), fn);
+}
+
+qmm_status qmm_gemv_lut(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z, qmm_half *Y,
+                        int64_t M, int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)
+{
+    const char *fn = "qmm_gemv_lut";
+    qmm_status st = check_shape(fn, M, K, N, bits, G, true);
+    if (st != QMM_OK) return st;
+    if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (M != 1 || bits != 1 || K > 8192)
+        return fail(QMM_ERR_UNSUPPORTED, "%s: implemented for M = 1, bits = 1, K <= 8192", fn);
+    qmm::GemvArgs a{X, wq, s, z, Y, (int)M, (int)K, (int)N, bits, (int)G};
+    return hip_status(qmm::launch_gemv_lut(a, (hipStream_t)stream), fn);
+}
+
 qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z, qmm_half *Y,
                     int64_t M, int64_t K, int64_t N, int bits, int64_t G, qmm_stream stream)
 {
@@ -119,14 +153,14 @@ qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s,
                        int64_t N, int fmt, int64_t G, qmm_stream stream)
 {
     const char *fn = "qmm_gemm_fp";
-    if (fmt != QMM_FP4_E2M1 && fmt != QMM_FP8_E4M3 && fmt != QMM_FP6_E3M2 && fmt != QMM_FP6_E2M3)
-        return fail(QMM_ERR_INVALID_ARG, "%s: unknown code format", fn);
-    const int bits = fmt == QMM_FP4_E2M1 ? 4 : fmt == QMM_FP8_E4M3 ? 8 : 6;
+    static const int kBits[] = {4, 8, 6, 6, 3, 5, 7};   // by format id (qmm.h)
+    if (fmt < QMM_FP4_E2M1 || fmt > QMM_FP7_E3M3) return fail(QMM_ERR_INVALID_ARG, "%s: unknown code format", fn);
+    const int bits = kBits[fmt];
     qmm_status st = check_shape(fn, M, K, N, bits, G, true);
     if (st != QMM_OK) return st;
     if (!X || !wq || !s || !Y) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
     qmm::GemvArgs a{X, wq, s, nullptr, Y, (int)M, (int)K, (int)N, bits, (int)G};
-    const int f = fmt;   // 0 E2M1, 1 E4M3, 2 E3M2, 3 E2M3
+    const int f = fmt;   // 0 E2M1, 1 E4M3, 2 E3M2, 3 E2M3, 4 E1M1, 5 E2M2, 6 E3M3
     if (M <= 16) {   // the decode kernels where they take the shape
         const hipError_t e = qmm::launch_gemv_fp(a, f, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e, fn);
@@ -175,6 +209,24 @@ qmm_status qmm_quantize(const qmm_half *W, uint8_t *codes, qmm_half *s, qmm_half
     return hip_status(qmm::launch_quantize(W, codes, s, z, (int)K, (int)N, bits, (int)G, (hipStream_t)stream), fn);
 }
 
+qmm_status qmm_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, int grid, qmm_stream stream)
+{
+    const char *fn = "qmm_probe_read";
+    if (!buf || !sink) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (bytes < 16 || bytes % 16 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: bytes must be a positive multiple of 16", fn);
+    if (grid < 1 || grid > 65535) return fail(QMM_ERR_INVALID_ARG, "%s: grid must be in 1..65535", fn);
+    return hip_status(qmm::launch_probe_read(buf, bytes, sink, grid, (hipStream_t)stream), fn);
+}
+
+qmm_status qmm_probe_mfma(float *sink, int iters, int grid, int shape, qmm_stream stream)
+{
+    const char *fn = "qmm_probe_mfma";
+    if (!sink) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (iters < 1 || grid < 1 || grid > 65535 || (shape != 0 && shape != 1))
+        return fail(QMM_ERR_INVALID_ARG, "%s: iters >= 1, grid in 1..65535, shape 0 or 1", fn);
+    return hip_status(qmm::launch_probe_mfma(sink, iters, grid, shape, (hipStream_t)stream), fn);
+}
+
 const char *qmm_status_string(qmm_status status)
 {
     switch (status) {
@@ -187,5 +239,7 @@ const char *qmm_status_string(qmm_status status)
 }
 
 const char *qmm_last_error(void) { return g_last_error; }
+
+const char *qmm_last_hip_error(void) { return g_last_error; }
 
 }  // extern "C"

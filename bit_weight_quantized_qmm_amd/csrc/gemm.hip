@@ -2,11 +2,11 @@
 //
 // f16 MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulation) on weights dequantised
 // in registers: each lane unpacks a whole 32-code run of one column into fp16
-// patterns 1024 + q 2^p and turns them into w' = (q - z) 2^p s with one exact
-// subtraction and one rounding multiply (BitLLM Sec. 2.2, eq. (5), per group).
-// The X tile goes through LDS, double-buffered, already permuted into the
-// run's half-slot order and scaled by 2^-p, so both MFMA operands are plain
-// 16-byte fragments.
+// patterns h = 1024 + q 2^p and turns them into w = (q - z) s: q - z by an
+// exact fp16 step (h 2^-p - (1024 2^-p + z)), then one rounding multiply
+// (BitLLM Sec. 2.2, eq. (5), per group).  The X tile goes through LDS,
+// double-buffered, permuted into the run's half-slot order (values
+// unchanged), so both MFMA operands are plain 16-byte fragments.
 //
 // Workgroup tile 128 (M) x 256 (N), 8 waves side by side in N, wave tile
 // 128 x 32 = 8 x 2 MFMA tiles; products too small to give every CU a
@@ -24,8 +24,10 @@
 
 namespace qmm {
 
+// 32 activations (natural order, two per dword) -> 16 half2 in the
+// half-slot order of RunPlan<BITS> (a permutation, no scaling).
 template <int BITS>
-__device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs)[16])
+__device__ __forceinline__ void x_perm_g(const uint32_t (&xr)[16], half2_t (&xs)[16])
 {
     using P = RunPlan<BITS>;
     _Float16 x[32];
@@ -40,12 +42,6 @@ __device__ __forceinline__ void x_slots_g(const uint32_t (&xr)[16], half2_t (&xs
         half2_t v;
         v[0] = x[P::code[2 * j]];
         v[1] = x[P::code[2 * j + 1]];
-        if (P::pos[2 * j] | P::pos[2 * j + 1]) {
-            half2_t sc;
-            sc[0] = (_Float16)pow2neg(P::pos[2 * j]);
-            sc[1] = (_Float16)pow2neg(P::pos[2 * j + 1]);
-            v = v * sc;
-        }
         xs[j] = v;
     }
 }
@@ -129,7 +125,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
             if constexpr (FMT == 0) {
-                x_slots_g<BITS>(raw[i], xs);
+                x_perm_g<BITS>(raw[i], xs);
             } else {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) xs[j] = as_half2(raw[i][j]);   // codes in order
@@ -213,20 +209,16 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * u + e;
-                    half2_t bias;
-                    half2_t p2;
-                    p2[0] = (_Float16)(float)(1u << P::pos[2 * j]);
-                    p2[1] = (_Float16)(float)(1u << P::pos[2 * j + 1]);
-                    if (PGZ) {
-                        half2_t k1;
-                        k1[0] = (_Float16)1024.0f;
-                        k1[1] = (_Float16)1024.0f;
-                        bias = z2 * p2 + k1;
-                    } else {
-                        bias[0] = (_Float16)(1024.0f + zdef * (float)(1u << P::pos[2 * j]));
-                        bias[1] = (_Float16)(1024.0f + zdef * (float)(1u << P::pos[2 * j + 1]));
-                    }
-                    const half2_t w = (as_half2(h[j]) - bias) * s2;
+                    // h = 1024 + q 2^p:  h 2^-p - (1024 2^-p + z) = q - z exactly in
+                    // fp16 (small integers and exact powers of two), then one
+                    // rounding multiply by s
+                    half2_t pinv, base;
+                    pinv[0] = (_Float16)pow2neg(P::pos[2 * j]);
+                    pinv[1] = (_Float16)pow2neg(P::pos[2 * j + 1]);
+                    base[0] = (_Float16)(1024.0f * pow2neg(P::pos[2 * j]) + (PGZ ? 0.0f : zdef));
+                    base[1] = (_Float16)(1024.0f * pow2neg(P::pos[2 * j + 1]) + (PGZ ? 0.0f : zdef));
+                    if (PGZ) base = base + z2;
+                    const half2_t w = (as_half2(h[j]) * pinv - base) * s2;
                     bq[ns][u][2 * e] = w[0];
                     bq[ns][u][2 * e + 1] = w[1];
                 }
@@ -332,14 +324,18 @@ hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)
     }
 }
 
-// Floating-point codes: fmt 0 = E2M1 (4-bit stream), fmt 1 = E4M3 (8-bit
-// stream); a.bits must match, a.z is ignored.
+// Floating-point codes: fmt 0 = E2M1 (4-bit stream), 1 = E4M3 (8-bit), 2 = E3M2
+// and 3 = E2M3 (6-bit), 4 = E1M1 (3-bit), 5 = E2M2 (5-bit), 6 = E3M3 (7-bit);
+// a.bits must match, a.z is ignored.
 hipError_t launch_gemm_fp(const GemvArgs &a, int fmt, hipStream_t st)
 {
     if (fmt == 0 && a.bits == 4) return gemm_dispatch<4, 1>(a, st);
     if (fmt == 1 && a.bits == 8) return gemm_dispatch<8, 2>(a, st);
     if (fmt == 2 && a.bits == 6) return gemm_dispatch<6, 3>(a, st);
     if (fmt == 3 && a.bits == 6) return gemm_dispatch<6, 4>(a, st);
+    if (fmt == 4 && a.bits == 3) return gemm_dispatch<3, 5>(a, st);
+    if (fmt == 5 && a.bits == 5) return gemm_dispatch<5, 6>(a, st);
+    if (fmt == 6 && a.bits == 7) return gemm_dispatch<7, 7>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -14,10 +14,40 @@ namespace qmm {
 
 // ---------------------------------------------------------------------------
 // The X side of one run: 32 activations (natural order, two per dword) ->
-// 16 half2 in the half-slot order of RunPlan<BITS>, slot s scaled by 2^-pos[s].
+// 16 half2 in the half-slot order of RunPlan<BITS>, slot s scaled by
+// 2^(e - pos[s]).  e is the exponent that brings the activation row's largest
+// magnitude into [128, 256) (row_exponent): the row is normalised before the
+// 2^-pos scaling, so no activation of normal size goes subnormal in fp16
+// however small the row is, the per-128-row sums of the MFMA GEMV stay below
+// 2^15, and the caller undoes 2^e on the fp32 result.  The product of the
+// two powers of two is formed in fp32 (exact), then each value is rounded
+// once to fp16.
 // ---------------------------------------------------------------------------
 template <int BITS>
-__device__ __forceinline__ void x_slots(const uint32_t (&xr)[16], half2_t (&xs)[16])
+__device__ __forceinline__ void x_slots_e(const uint32_t (&xr)[16], half2_t (&xs)[16], int e)
+{
+    using P = RunPlan<BITS>;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const half2_t p = as_half2(xr[i]);
+        x[2 * i] = (float)p[0];
+        x[2 * i + 1] = (float)p[1];
+    }
+    const float f = __builtin_ldexpf(1.0f, e);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        half2_t v;
+        v[0] = (_Float16)(x[P::code[2 * j]] * (f * pow2neg(P::pos[2 * j])));
+        v[1] = (_Float16)(x[P::code[2 * j + 1]] * (f * pow2neg(P::pos[2 * j + 1])));
+        xs[j] = v;
+    }
+}
+
+// The X side without scaling: 32 activations permuted into the slot order,
+// for kernels whose B operand is (q - z) s itself.
+template <int BITS>
+__device__ __forceinline__ void x_perm(const uint32_t (&xr)[16], half2_t (&xs)[16])
 {
     using P = RunPlan<BITS>;
     _Float16 x[32];
@@ -32,14 +62,66 @@ __device__ __forceinline__ void x_slots(const uint32_t (&xr)[16], half2_t (&xs)[
         half2_t v;
         v[0] = x[P::code[2 * j]];
         v[1] = x[P::code[2 * j + 1]];
-        if (P::pos[2 * j] | P::pos[2 * j + 1]) {
-            half2_t sc;
-            sc[0] = (_Float16)pow2neg(P::pos[2 * j]);
-            sc[1] = (_Float16)pow2neg(P::pos[2 * j + 1]);
-            v = v * sc;
-        }
         xs[j] = v;
     }
+}
+
+// Largest |x| of the fp16 values in a run's 16 dwords, as a 15-bit magnitude
+// pattern (patterns of finite non-negative fp16 values order like the values).
+__device__ __forceinline__ uint32_t run_absmax_bits(const uint32_t (&xr)[16])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, max(xr[i] & 0x7fffu, (xr[i] >> 16) & 0x7fffu));
+    return m;
+}
+
+template <int CTRL, int ROWM, int BANKM, bool BC>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWM, BANKM, BC));
+}
+
+// Maximum over the 64 lanes of a wave (DPP, as wave_sum_dpp), in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = dpp_max<0xB1, 0xF, 0xF, true>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E, 0xF, 0xF, true>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max<0x141, 0xF, 0xF, true>(v);   // row_half_mirror
+    v = dpp_max<0x140, 0xF, 0xF, true>(v);   // row_mirror
+    v = dpp_max<0x142, 0xA, 0xF, false>(v);  // row_bcast:15
+    v = dpp_max<0x143, 0xC, 0xF, false>(v);  // row_bcast:31: lane 63 holds the maximum
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// e such that the row maximum |x| (given as its fp16 magnitude pattern) times
+// 2^e lies in [128, 256); 8 for an all-zero row (any value would do).
+__device__ __forceinline__ int row_exponent(uint32_t maxbits)
+{
+    return 8 - __builtin_amdgcn_frexp_expf((float)as_half((uint16_t)maxbits));
+}
+
+// (1024 * 2^-pos + zc) for both halves of slot pair j: with h = 1024 + q 2^pos,
+// h * 2^-pos - that = q - zc exactly in fp16 (all terms are small integers
+// or exact powers of two).
+template <int BITS>
+__device__ __forceinline__ half2_t slot_base(int j, float zc)
+{
+    using P = RunPlan<BITS>;
+    half2_t b;
+    b[0] = (_Float16)(1024.0f * pow2neg(P::pos[2 * j]) + zc);
+    b[1] = (_Float16)(1024.0f * pow2neg(P::pos[2 * j + 1]) + zc);
+    return b;
+}
+
+template <int BITS>
+__device__ __forceinline__ half2_t slot_pow2neg(int j)
+{
+    using P = RunPlan<BITS>;
+    half2_t b;
+    b[0] = (_Float16)pow2neg(P::pos[2 * j]);
+    b[1] = (_Float16)pow2neg(P::pos[2 * j + 1]);
+    return b;
 }
 
 // Per-slot constant of the fp16 code pattern: (1024 + zc * 2^pos) for a fixed
@@ -99,24 +181,27 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
     return v;
 }
 
-template <int BITS, int RPL, int D, int IPT, bool PGZ, int FMT = 0>
-__global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
-                                                      const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
-                                                      uint16_t *__restrict__ Y, int K, int N, int G)
+// The workgroup is number wg of the nwg that share the product's columns
+// (the whole grid for qmm_gemv; a slice of it in a grouped launch).
+template <int BITS, int RPL, int D, int IPT, bool PGZ, int FMT>
+__device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+                                        const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
+                                        uint16_t *__restrict__ Y, int K, int N, int G, int wg, int nwg)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int R = K >> 5, ng = K / G;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     // waves sweep the columns together: wave w takes w, w + W, w + 2W, ...
-    const int W = (int)gridDim.x * 4;
-    const int w = (int)blockIdx.x * 4 + wave;
+    const int W = nwg * 4;
+    const int w = wg * 4 + wave;
     const int ncw = w < N ? (N - 1 - w) / W + 1 : 0;    // columns of this wave (<= 64)
 
-    // LDS: xs [R] runs x 64 B | 64 B zeros | 64 B dummy | c1 [R] + 4 | c2 [R] + 4 (PGZ)
+    // LDS: xs [R] runs x 64 B | 64 B zeros | 64 B dummy | c1 [R] + 4 | c2 [R] + 4 (PGZ) | rmax [4]
     const uint32_t xs_bytes = (uint32_t)R * 64u;
     float *c1 = reinterpret_cast<float *>(smem + xs_bytes + 128);
     float *c2 = c1 + R + 4;
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(c2 + (PGZ ? R + 4 : 0));
 
     // 1. activations for the staging (IPT runs per thread)
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)K * 2u);
@@ -162,11 +247,22 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
     for (int q = 0; q < D; ++q) issue(q, q);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. staging: waves that own items convert X to slot order with bias sums
+    // 3. staging: waves that own items convert X to slot order with bias sums,
+    //    the row first normalised by 2^e (x_slots_e); float codes keep X as is
     const float zdef = (float)(1u << (BITS - 1));
 #pragma unroll
     for (int i = 0; i < IPT; ++i) asm volatile("" ::"v"(raw[i][0]), "v"(raw[i][15]));   // keep the loads here
     if (tid < 4) reinterpret_cast<int4_t *>(smem + xs_bytes)[tid] = int4_t{0, 0, 0, 0};
+    int e = 0;
+    if constexpr (FMT == 0) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) mx = max(mx, run_absmax_bits(raw[i]));   // zeros past K
+        mx = wave_max_u32(mx);
+        if (lane == 0) rmax[wave] = mx;
+        __syncthreads();
+        e = row_exponent(max(max(rmax[0], rmax[1]), max(rmax[2], rmax[3])));
+    }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         if (256 * i + 64 * wave < R) {               // wave-uniform
@@ -178,7 +274,7 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
 #pragma unroll
                 for (int p = 0; p < 16; ++p) xs[p] = as_half2(raw[i][p]);
             } else {
-                x_slots<BITS>(raw[i], xs);
+                x_slots_e<BITS>(raw[i], xs, e);
             }
 #pragma unroll
             for (int p = 0; p < 16 && FMT == 0; ++p) {
@@ -257,18 +353,59 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
             }
         }
     }
-    if (lane < ncw) Y[w + lane * W] = f32_to_f16_bits(yout);
+    if (lane < ncw) Y[w + lane * W] = f32_to_f16_bits(yout * __builtin_ldexpf(1.0f, -e));
+}
+
+template <int BITS, int RPL, int D, int IPT, bool PGZ, int FMT = 0>
+__global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
+                                                      const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
+                                                      uint16_t *__restrict__ Y, int K, int N, int G)
+{
+    m1_body<BITS, RPL, D, IPT, PGZ, FMT>(X, wq, s, z, Y, K, N, G, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Columns in flight per wave for RPL runs per lane (the fastest measured:
+// 8 / 4 / 2 / 1 for RPL 1 / 2 / 4 / 8; 4 for RPL 4 at k <= 2, whose columns
+// carry few bytes) and items of X staging per thread.
+__host__ __device__ constexpr int m1_depth(int bits, int rpl) { return rpl <= 1 ? 8 : rpl == 2 ? 4 : rpl == 4 ? (bits <= 2 ? 4 : 2) : 1; }
+__host__ __device__ constexpr int m1_ipt(int rpl) { return rpl == 8 ? 2 : 1; }
+
+// Several M = 1 products in one launch (qmm_gemv_grouped): workgroups
+// wg0[p] .. wg0[p + 1] - 1 serve problem p, each running the decode body above
+// for that problem's code width, so all problems stream at once over their
+// own share of the CUs and the launch's start-up and drain are paid once.
+template <int RPL>
+__global__ __launch_bounds__(256) void gemv_m1_grouped_kernel(const GroupArgs a)
+{
+    int p = 0;
+    while (p + 1 < a.count && (int)blockIdx.x >= a.wg0[p + 1]) ++p;   // wave-uniform
+    const GroupProblem g = a.p[p];
+    const int wg = (int)blockIdx.x - a.wg0[p], nwg = a.wg0[p + 1] - a.wg0[p];
+    constexpr int IPT = m1_ipt(RPL);
+#define QMM_GB(B)                                                                                                    \
+    case 2 * B:                                                                                                      \
+        m1_body<B, RPL, m1_depth(B, RPL), IPT, false, 0>(g.X, g.wq, g.s, g.z, g.Y, a.K, g.N, a.G, wg, nwg);          \
+        break;                                                                                                       \
+    case 2 * B + 1:                                                                                                  \
+        m1_body<B, RPL, m1_depth(B, RPL), IPT, true, 0>(g.X, g.wq, g.s, g.z, g.Y, a.K, g.N, a.G, wg, nwg);           \
+        break;
+    switch (2 * g.bits + (g.z != nullptr ? 1 : 0)) {
+        QMM_GB(1) QMM_GB(2) QMM_GB(3) QMM_GB(4) QMM_GB(5) QMM_GB(6) QMM_GB(7) QMM_GB(8)
+        default: break;
+    }
+#undef QMM_GB
 }
 
 // ---------------------------------------------------------------------------
 // 2 <= M <= 16 (and M = 1 with very long K): f16 MFMA 16x16x32, M padded to 16.
 // A workgroup of 8 waves owns one 16-column tile at a time; the waves split K.
 // In a K step of 128 rows, lane group g (lanes 16g..16g+15) owns run 4t+g of
-// column (lane % 16): it unpacks the run to fp16 patterns, dequantises them in
-// registers to w' = (q - z) 2^p s (exact subtraction, one rounding), and feeds
-// four MFMAs.  The A operand holds X rows in the same slot order, pre-scaled
-// by 2^-p, and stays in VGPRs across column tiles.  Partial tiles of the 8
-// waves are summed through LDS in a fixed order.
+// column (lane % 16): it unpacks the run to fp16 patterns h = 1024 + q 2^p,
+// dequantises them in registers to w = (h 2^-p - (1024 2^-p + z)) s = (q - z) s
+// (exact difference, one rounding), and feeds four MFMAs.  The A operand holds
+// X rows permuted into the same slot order (unscaled) and stays in VGPRs
+// across column tiles.  Partial tiles of the 8 waves are summed through LDS in
+// a fixed order.
 // ---------------------------------------------------------------------------
 template <int BITS, int T, bool PGZ>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
@@ -317,7 +454,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
                     const uint32_t off = (run < R && c < M) ? ((uint32_t)c * K + (uint32_t)run * 32u) * 2u : OOB;
                     load_dwords<LOAD_DEFAULT>(xr, off, raw, 16);
                     half2_t xs[16];
-                    x_slots<BITS>(raw, xs);
+                    x_perm<BITS>(raw, xs);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         half8_t v;
@@ -347,16 +484,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * u + e;
-                        half2_t bias;
-                        if (PGZ) {
-                            half2_t k1;
-                            k1[0] = (_Float16)1024.0f;
-                            k1[1] = (_Float16)1024.0f;
-                            bias = z2 * slot_pow2<BITS>(j) + k1;
-                        } else {
-                            bias = slot_bias<BITS>(j, zdef);
-                        }
-                        const half2_t w = (as_half2(h[j]) - bias) * s2;
+                        // h 2^-pos - (1024 2^-pos + z) = q - z exactly; one rounding multiply by s
+                        const half2_t base = PGZ ? slot_base<BITS>(j, 0.f) + z2 : slot_base<BITS>(j, zdef);
+                        const half2_t w = (as_half2(h[j]) * slot_pow2neg<BITS>(j) - base) * s2;
                         b[2 * e] = w[0];
                         b[2 * e + 1] = w[1];
                     }
@@ -411,7 +541,7 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 
     // LDS: xs [M][R4] runs x 64 B | 64 B zeros | 64 B dummy | c1 [M][R4] + 4 dummy |
     //      c2 [M][R4] + 4 dummy (PGZ) | sl [16][ng] + 8 dummy | zl [16][ng] + 8 dummy (PGZ) |
-    //      red [ks][4][16].  Staging threads without an item write the dummy slots, so the
+    //      red [ks][4][16] | rmax [4].  Staging threads without an item write the dummy slots, so the
     //      staging code has no branches (a branch would let the compiler sink the
     //      activation loads behind the weight loads, and loads complete in order).
     const uint32_t xs_bytes = (uint32_t)M * R4 * 64u;
@@ -460,7 +590,17 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    // 4. stage X in slot order with its per-run bias sums; scales; zero pad
+    // 4. per-row maximum |x| (every row normalised by its own 2^e, undone at the end)
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(red + ks * 4 * 16);
+    if (tid < 4) rmax[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it0 = tid + i * nthreads;
+        atomicMax(&rmax[min(it0 / R4, 3)], it0 < M * R4 ? run_absmax_bits(raw[i]) : 0u);
+    }
+    __syncthreads();
+    // 5. stage X in slot order with its per-run bias sums; scales; zero pad
     const float zdef = (float)(1u << (BITS - 1));
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -468,7 +608,7 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
         const int it = it0 < M * R4 ? it0 : M * R4;   // M * R4 = the dummy item
         {
             half2_t xs[16];
-            x_slots<BITS>(raw[i], xs);
+            x_slots_e<BITS>(raw[i], xs, row_exponent(rmax[min(it0 / R4, M - 1)]));
             float a1 = 0.f, a2 = 0.f;
 #pragma unroll
             for (int p = 0; p < 16; ++p) {
@@ -501,7 +641,7 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
     if (tid < 4) reinterpret_cast<int4_t *>(smem + xs_bytes)[tid] = int4_t{0, 0, 0, 0};
     __syncthreads();
 
-    // 5. K steps: 4 dependent MFMAs per step, the run bias as the accumulator's
+    // 6. K steps: 4 dependent MFMAs per step, the run bias as the accumulator's
     //    start value.  Rule kept throughout: no load is issued while a chain is in
     //    flight.  The LDS operands of step t+1 are read before chain t starts (so
     //    they cannot land in registers chain t still reads), and chain t's result is
@@ -554,6 +694,11 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
         __builtin_amdgcn_sched_barrier(0);
         uint32_t h[16];
         run_to_half2<BITS>(d[t], h);
+        // The unpack's v_and_or_b32 is inline asm, which the compiler does not
+        // count as a VALU write when it spaces an MFMA that reads the result:
+        // fence the unpack off and give the MFMAs explicit wait states.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7");
         float4_t acc = cur.init;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -572,13 +717,14 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
         cur = nxt;
     }
 
-    // 6. fixed-order sum over the ks waves
+    // 7. fixed-order sum over the ks waves, the row's 2^e undone
     if (om < M) red[(wave * 4 + om) * 16 + c] = y;
     __syncthreads();
     if (tid < M * 16) {
         const int m = tid >> 4, cc = tid & 15;
         float v = 0.f;
         for (int w = 0; w < ks; ++w) v += red[(w * 4 + m) * 16 + cc];
+        v *= __builtin_ldexpf(1.0f, -row_exponent(rmax[m]));
         if (cc < nvalid) Y[(size_t)m * N + n0 + cc] = f32_to_f16_bits(v);
     }
 }
@@ -626,6 +772,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     // the odd row stride keeps the transposing writes free of bank conflicts
     constexpr int SZW = T * 16 + 1;
     __shared__ uint32_t sz[MMA_MAXNG * SZW];
+    __shared__ uint32_t rmx[MMA_WAVES][16];   // per wave, per row: max |x| over the wave's K slice
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
@@ -682,13 +829,31 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     };
 
     // A fragments and correction fragments of the wave's K slice, once: they
-    // do not depend on the column tile.
+    // do not depend on the column tile.  Row c is first normalised by 2^e (its
+    // maximum |x| over all of K taken across the 8 waves), so S1 and S2 stay
+    // below 2^15 and fit the fp16 high part; 2^e is undone on the output.
     half8_t A[S][4];
     uint32_t AC[S][2];   // correction fragment of lane group 0: (S1 hi, S1 lo), (S2 hi, S2 lo)
     {
         uint32_t xa[S][16];
 #pragma unroll
         for (int st = 0; st < S; ++st) load_xrun(wave * S + st, xa[st]);
+        int erow = 0;
+        if constexpr (FMT == 0) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int st = 0; st < S; ++st) mx = max(mx, run_absmax_bits(xa[st]));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+            if (g == 0) rmx[wave][c] = mx;
+        }
+        __syncthreads();   // also orders the s | z table writes before the loop's reads
+        if constexpr (FMT == 0) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int w = 0; w < MMA_WAVES; ++w) mx = max(mx, rmx[w][c]);
+            erow = row_exponent(mx);
+        }
 #pragma unroll
         for (int st = 0; st < S; ++st) {
             half2_t xs[16];
@@ -696,7 +861,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
                 for (int p = 0; p < 16; ++p) xs[p] = as_half2(xa[st][p]);
             } else {
-                x_slots<BITS>(xa[st], xs);
+                x_slots_e<BITS>(xa[st], xs, erow);
             }
             half2_t one2;
             one2[0] = (_Float16)1.0f;
@@ -719,6 +884,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
             s1 += __shfl_xor(s1, 32);
             s2 += __shfl_xor(s2, 16);
             s2 += __shfl_xor(s2, 32);
+            s2 = __builtin_ldexpf(s2, erow);   // sum of x 2^e (exact scaling)
             const _Float16 s1h = (_Float16)s1, s2h = (_Float16)s2;
             const _Float16 s1l = (_Float16)(s1 - (float)s1h), s2l = (_Float16)(s2 - (float)s2h);
             half2_t p1, p2;
@@ -730,7 +896,6 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
             AC[st][1] = g == 0 ? as_u32(p2) : 0u;
         }
     }
-    __syncthreads();
 
     // UT tiles per loop iteration keep every ring slot a compile-time index
     constexpr int UT = D > S ? D / S : 1;
@@ -815,6 +980,12 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
         for (int w = 0; w < MMA_WAVES; ++w) v += red[w][j][l][i];
         const int n = 16 * (tile0 + j) + col;
+        if constexpr (FMT == 0) {   // undo the row's 2^e
+            uint32_t mx = 0;
+#pragma unroll
+            for (int w = 0; w < MMA_WAVES; ++w) mx = max(mx, rmx[w][m]);
+            v *= __builtin_ldexpf(1.0f, -row_exponent(mx));
+        }
         if (m < M && n < N) Y[(size_t)m * N + n] = f32_to_f16_bits(v);
     }
 }
@@ -864,7 +1035,7 @@ static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
 static size_t m1_lds_bytes(int K, bool pgz)
 {
     const int R = K / 32;
-    return (size_t)R * 64 + 128 + 4u * (size_t)(R + 4) * (pgz ? 2 : 1);
+    return (size_t)R * 64 + 128 + 4u * (size_t)(R + 4) * (pgz ? 2 : 1) + 16;
 }
 
 // Workgroups for the M = 1 stream: one per CU (four waves, one per SIMD),
@@ -911,10 +1082,61 @@ static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
 {
     const int R = a.K / 32;
     const int rpl_need = (R + 63) / 64;
-    if (rpl_need <= 1) return gemv_m1_go<BITS, 1, 8, 1, PGZ>(a, st);
-    if (rpl_need <= 2) return gemv_m1_go<BITS, 2, 4, 1, PGZ>(a, st);
-    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, (BITS <= 2 ? 4 : 2), 1, PGZ>(a, st);
-    return gemv_m1_go<BITS, 8, 1, 2, PGZ>(a, st);
+    if (rpl_need <= 1) return gemv_m1_go<BITS, 1, m1_depth(BITS, 1), m1_ipt(1), PGZ>(a, st);
+    if (rpl_need <= 2) return gemv_m1_go<BITS, 2, m1_depth(BITS, 2), m1_ipt(2), PGZ>(a, st);
+    if (rpl_need <= 4) return gemv_m1_go<BITS, 4, m1_depth(BITS, 4), m1_ipt(4), PGZ>(a, st);
+    return gemv_m1_go<BITS, 8, m1_depth(BITS, 8), m1_ipt(8), PGZ>(a, st);
+}
+
+// Grouped M = 1 products: the CUs are shared out in proportion to each
+// problem's estimated time (packed bytes plus a per-code compute share), at
+// least one workgroup each and enough that no wave takes more than 64 columns.
+template <int RPL>
+static hipError_t grouped_go(const GroupArgs &ga, int grid, hipStream_t st)
+{
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_m1_grouped_kernel<RPL>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemv_m1_grouped_kernel<RPL>), dim3(grid), dim3(256), m1_lds_bytes(ga.K, true), st, ga);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_grouped(const GroupArgs &in, hipStream_t st)
+{
+    GroupArgs ga = in;
+    const int n = ga.count, cus = num_cus();
+    double cost[QMM_GROUP_MAX], total = 0.0;
+    for (int p = 0; p < n; ++p) {
+        cost[p] = (double)ga.p[p].N * ((double)ga.p[p].bits + 1.5);
+        total += cost[p];
+    }
+    int nwg[QMM_GROUP_MAX], sum = 0, big = 0;
+    for (int p = 0; p < n; ++p) {
+        const int need = (ga.p[p].N + 255) / 256;   // 4 waves x at most 64 columns each
+        nwg[p] = std::max(need, std::max(1, (int)(cus * cost[p] / total + 0.5)));
+        sum += nwg[p];
+        if (cost[p] > cost[big]) big = p;
+    }
+    if (sum > cus) {   // trim the largest share while it keeps its minimum
+        const int need = (ga.p[big].N + 255) / 256;
+        const int cut = std::min(sum - cus, nwg[big] - std::max(1, need));
+        nwg[big] -= cut;
+        sum -= cut;
+    } else if (sum < cus) {
+        nwg[big] += cus - sum;
+        sum = cus;
+    }
+    ga.wg0[0] = 0;
+    for (int p = 0; p < n; ++p) ga.wg0[p + 1] = ga.wg0[p] + nwg[p];
+    const int rpl = (ga.K / 32 + 63) / 64;
+    if (rpl <= 1) return grouped_go<1>(ga, sum, st);
+    if (rpl <= 2) return grouped_go<2>(ga, sum, st);
+    if (rpl <= 4) return grouped_go<4>(ga, sum, st);
+    return grouped_go<8>(ga, sum, st);
 }
 
 template <int BITS, bool PGZ>
@@ -948,7 +1170,7 @@ static size_t rows_lds_bytes(int M, int K, int G, int ks, bool pgz)
     size_t b = (size_t)M * R4 * 64 + 128 + 4u * (size_t)(M * R4 + 4) * (pgz ? 2 : 1) +
                2u * (size_t)(16 * ng + 8) * (pgz ? 2 : 1);
     b = (b + 15) & ~(size_t)15;
-    return b + (size_t)ks * 4 * 16 * 4;
+    return b + (size_t)ks * 4 * 16 * 4 + 16;
 }
 
 template <int BITS, int T, int IPT, int SPT, bool G128, bool PGZ>
@@ -1041,6 +1263,9 @@ hipError_t launch_gemv_fp(const GemvArgs &a, int fmt, hipStream_t st)
     if (fmt == 1 && a.bits == 8) return gemv_small_fp<8, 2>(a, st);
     if (fmt == 2 && a.bits == 6) return gemv_small_fp<6, 3>(a, st);
     if (fmt == 3 && a.bits == 6) return gemv_small_fp<6, 4>(a, st);
+    if (fmt == 4 && a.bits == 3) return gemv_small_fp<3, 5>(a, st);
+    if (fmt == 5 && a.bits == 5) return gemv_small_fp<5, 6>(a, st);
+    if (fmt == 6 && a.bits == 7) return gemv_small_fp<7, 7>(a, st);
     return hipErrorInvalidValue;
 }
 

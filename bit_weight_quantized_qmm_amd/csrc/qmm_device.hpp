@@ -119,14 +119,79 @@ __device__ __forceinline__ half2_t fp_code_pair(const uint32_t *d, int j)
     }
 }
 
+// 32 bits of a run's stream starting at bit b (compile-time after unrolling);
+// only the low `width` bits are used by the caller.
+template <int BITS>
+__device__ __forceinline__ uint32_t run_window(const uint32_t (&d)[BITS], int b, int width)
+{
+    const int i = b >> 5, sh = b & 31;
+    if (sh == 0) return d[i];
+    if (sh + width <= 32 || i + 1 >= BITS) return d[i] >> sh;
+    return __builtin_amdgcn_alignbit(d[i + 1], d[i], (uint32_t)sh);
+}
+
+// 3-, 5- and 7-bit float codes (FMT 5: E1M1, 6: E2M2, 7: E3M3) have no
+// conversion instruction of their own.  Each code is moved into a container
+// format that has one, with the exponent widened by leading zero bits and the
+// sign moved to the container's sign bit: E1M1 -> E2M1 nibble, E2M2 -> E5M2
+// byte, E3M3 -> E4M3 byte.  Field by field, the container then encodes the
+// code's value times 2^(container bias - code bias) (subnormals included:
+// both formats put the leading zero exponent at the same place), so the
+// converter's scale operand 2^(code bias - container bias) gives the exact
+// value: 2, 2^14 and 2^4.  Spreading the k-bit fields to 4- or 8-bit lanes
+// takes two mask-and-shift steps (halves, then single codes), the sign move a
+// third.
+template <int FMT, int BITS>
+__device__ __forceinline__ void fp_small_run_to_half2(const uint32_t (&d)[BITS], uint32_t (&h)[16])
+{
+    if constexpr (FMT == 5) {       // E1M1: 8 codes (24 bits) -> 8 E2M1 nibbles per dword
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            const uint32_t x = run_window<BITS>(d, 24 * o, 24);
+            uint32_t t = (x & 0x000fffu) | ((x & 0xfff000u) << 4);
+            t = (t & 0x003f003fu) | ((t & 0x0fc00fc0u) << 2);
+            t = (t & 0x07070707u) | ((t & 0x38383838u) << 1);
+            t = (t & 0x33333333u) | ((t & 0x44444444u) << 1);
+            h[4 * o + 0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, 2.0f, 0));
+            h[4 * o + 1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, 2.0f, 1));
+            h[4 * o + 2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, 2.0f, 2));
+            h[4 * o + 3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, 2.0f, 3));
+        }
+    } else if constexpr (FMT == 6) {   // E2M2: 4 codes (20 bits) -> 4 E5M2 bytes per dword
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+            const uint32_t x = run_window<BITS>(d, 20 * o, 20);
+            uint32_t t = (x & 0x003ffu) | ((x & 0xffc00u) << 6);
+            t = (t & 0x001f001fu) | ((t & 0x03e003e0u) << 3);
+            t = (t & 0x0f0f0f0fu) | ((t & 0x10101010u) << 3);
+            h[2 * o + 0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(t, 16384.0f, false));
+            h[2 * o + 1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(t, 16384.0f, true));
+        }
+    } else {                            // E3M3: 4 codes (28 bits) -> 4 E4M3 bytes per dword
+        static_assert(FMT == 7, "float code format");
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+            const uint32_t x = run_window<BITS>(d, 28 * o, 28);
+            uint32_t t = (x & 0x0003fffu) | ((x & 0xfffc000u) << 2);
+            t = (t & 0x007f007fu) | ((t & 0x3f803f80u) << 1);
+            t = (t & 0x3f3f3f3fu) | ((t & 0x40404040u) << 1);
+            h[2 * o + 0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 16.0f, false));
+            h[2 * o + 1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 16.0f, true));
+        }
+    }
+}
+
 // A whole run of floating-point codes as 16 fp16 pairs (pair p = codes 2p and
-// 2p + 1, exact values): per pair for E2M1 / E4M3, and one packed conversion
-// of all 32 codes for the 6-bit formats (FMT 3: E3M2, 4: E2M3), whose source
-// is the run's 6 dwords in stream order.
+// 2p + 1, exact values): per pair for E2M1 / E4M3, one packed conversion of
+// all 32 codes for the 6-bit formats (FMT 3: E3M2, 4: E2M3), whose source is
+// the run's 6 dwords in stream order, and through a container format for the
+// 3-, 5- and 7-bit ones (FMT 5..7).
 template <int FMT, int BITS>
 __device__ __forceinline__ void fp_run_to_half2(const uint32_t (&d)[BITS], uint32_t (&h)[16])
 {
-    if constexpr (FMT == 3 || FMT == 4) {
+    if constexpr (FMT >= 5) {
+        fp_small_run_to_half2<FMT, BITS>(d, h);
+    } else if constexpr (FMT == 3 || FMT == 4) {
         static_assert(BITS == 6, "6-bit float codes");
         typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
         typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));

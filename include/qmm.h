@@ -46,7 +46,10 @@
  *   G >= 32, G % 32 == 0 and K % G == 0 (no 32-code run straddles a group);
  *   N >= 1; M >= 1; required pointers non-NULL.
  *   Device pointers must be 4-byte aligned (Wq, X, Y: 16-byte aligned is fastest).
- *   Scales must keep |s| * 2^10 finite in fp16 (|s| < 64) on the MFMA paths.
+ *   Scales must keep |s| * |q - z| finite in fp16 (|s| < 256 always does).
+ *   X: any finite fp16 values; each activation row is brought to a common
+ *   power-of-two range inside the kernels and the factor is undone on the
+ *   fp32 result, so the precision does not depend on the scale of X.
  */
 #ifndef QMM_H_
 #define QMM_H_
@@ -68,8 +71,12 @@ typedef enum qmm_status {
 typedef void *qmm_stream;       /* hipStream_t */
 typedef uint16_t qmm_half;      /* IEEE binary16 bit pattern */
 
-/* Bytes of the packed stream for K x N codes of `bits` bits: N*K*bits/8.
- * Returns 0 for invalid shapes.  Pure host function. */
+/* Bytes of the packed stream for K x N codes of `bits` bits: N*K*bits/8, the
+ * contiguous packing of BitLLM Sec. 4.3 ("Quantization-Aware Packing", Fig. 8(a):
+ * eight 4-bit values fill one 32-bit word, so k-bit codes take k/32 of a word
+ * each, with no padding).  Returns 0 for invalid shapes (bits outside 1..8,
+ * negative sizes, K*bits not a whole number of bytes).  Pure host function:
+ * no pointer, no HIP call. */
 size_t qmm_packed_bytes(int64_t K, int64_t N, int bits);
 
 /* Pack codes [K][N] (low `bits` bits of each byte) into Wq [N][K*bits/32].
@@ -92,7 +99,13 @@ qmm_status qmm_pack_signed(const int8_t *codes, uint32_t *wq, int64_t K, int64_t
 
 /* Test hook: decode Wq back to codes [K][N] with the same in-register unpack
  * (dword runs -> fp16 bit patterns) that qmm_gemv and qmm_gemm use, then read
- * each code back out of its fp16 pattern.  Exact inverse of qmm_pack. */
+ * each code back out of its fp16 pattern.  Exact inverse of qmm_pack: the
+ * register reinterpretation of a packed bit string without a shared-memory
+ * layout conversion (the Tilus verdict page, pith extraction core discovery:
+ * LoadGlobal -> View -> Cast; BitLLM Sec. 4.3, Fig. 8(a) for the bit order).
+ *   wq     device, uint32 [N][K*bits/32] (read)
+ *   codes  device, uint8 [K][N] (written: code values 0..2^bits-1)
+ * Shape errors as for qmm_pack; enqueued on stream, no allocation. */
 qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, int bits,
                       qmm_stream stream);
 
@@ -114,10 +127,62 @@ qmm_status qmm_gemv(const qmm_half *X, const uint32_t *wq, const qmm_half *s, co
                     qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
                     qmm_stream stream);
 
-/* Same arguments and result as qmm_gemv for any M >= 1: f16 MFMA (fp32
- * accumulation) on weights dequantised in registers ((q - z) 2^p formed by an
- * exact fp16 subtraction, then one rounding multiply by s), X staged through
- * LDS in 128 x 256 output tiles.  Intended for large M (prefill). */
+/* One M = 1 product of a grouped launch (qmm_gemv_grouped).  Device pointers
+ * as in qmm_gemv: X fp16 [1][K], wq [N][K*bits/32], s and z fp16 [N][K/G]
+ * (z may be NULL: 2^(bits-1)), Y fp16 [1][N]. */
+typedef struct qmm_gemv_problem {
+    const qmm_half *X;
+    const uint32_t *wq;
+    const qmm_half *s;
+    const qmm_half *z;
+    qmm_half *Y;
+    int64_t N;
+    int bits;
+} qmm_gemv_problem;
+
+/* Several decode products in one launch: for each p < count, Y_p = X_p .
+ * dequant(Wq_p) with w = (q - z) s per group (BitLLM Sec. 2.2, eq. (5)),
+ * exactly what qmm_gemv computes for that problem alone with M = 1 (the same
+ * kernel body, bit for bit).  The problems share K and G; N, the code width
+ * and every array are their own.  The launch splits the GPU's CUs between
+ * the problems in proportion to their work, so all of them stream at once
+ * and the kernel start-up and drain are paid once for the group (a decode
+ * step runs several such products per layer).
+ *   probs  HOST array of count descriptors (read during the call only)
+ *   count  1..16;  K, G as for qmm_gemv (K <= 16384)
+ * Errors: QMM_ERR_INVALID_ARG for a bad count, a null pointer in a
+ * descriptor or a shape qmm_gemv would reject; QMM_ERR_UNSUPPORTED for
+ * K > 16384 or a problem whose weights reach 2 GiB.  Outputs of different
+ * problems must not overlap. */
+qmm_status qmm_gemv_grouped(const qmm_gemv_problem *probs, int count, int64_t K, int64_t G,
+                            qmm_stream stream);
+
+/* Decode product for 1-bit codes by table lookup (the T-MAC style of BitLLM
+ * Sec. 8, Related Work, and the unpack-cost accounting of Sec. 1 / Fig. 5 it
+ * targets): the same result as qmm_gemv, Y = X . dequant(Wq) with
+ * w = (q - z) s (Sec. 2.2, eq. (5)), computed without unpacking the codes.  For
+ * every 4 consecutive rows of K the workgroup builds, in LDS, the 16 partial
+ * sums of those 4 activations (fp32); each 4-bit nibble of a column's stream
+ * is then one table read, and per 32-code run
+ *   y += s (sum of the run's 8 reads - z * sum of the run's 32 activations).
+ * Arguments, layouts, ownership and errors as for qmm_gemv; implemented for
+ * M == 1, bits == 1, K <= 8192 and N <= 256 * (CU count), i.e. N <= 65536 on
+ * a 256-CU part (QMM_ERR_UNSUPPORTED otherwise). */
+qmm_status qmm_gemv_lut(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
+                        qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
+                        qmm_stream stream);
+
+/* Prefill-shaped product: Y = X . dequant(Wq) for any M >= 1, with
+ * w = (q - z) s per (column, group) as in BitLLM Sec. 2.2, eq. (5), and the
+ * dequantisation done in registers right before the tensor-core product (the
+ * Tilus verdict page, pith extraction core discovery and forward implications:
+ * LoadGlobal -> View -> Cast feeding MMA).  f16 MFMA with fp32 accumulation;
+ * each weight becomes q - z by an exact fp16 operation and then (q - z) s by
+ * one rounding multiply, so codes equal to their zero-point give exact zeros.
+ * X (unscaled) is staged through LDS in 128 x 256 output tiles.
+ *   X   device, fp16 [M][K];  wq, s, z as for qmm_gemv;  Y device, fp16 [M][N]
+ * Preconditions and errors as for qmm_gemv without the M <= 16 limit;
+ * |s| * |q - z| must be finite in fp16 (|s| < 256 always is). */
 qmm_status qmm_gemm(const qmm_half *X, const uint32_t *wq, const qmm_half *s, const qmm_half *z,
                     qmm_half *Y, int64_t M, int64_t K, int64_t N, int bits, int64_t G,
                     qmm_stream stream);
@@ -130,7 +195,13 @@ enum {
     QMM_FP8_E4M3 = 1,   /* 8-bit stream: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0..448,
                            codes 0x7F / 0xFF (NaN) are not valid weights */
     QMM_FP6_E3M2 = 2,   /* 6-bit stream: sign, 3 exponent bits (bias 3), 2 mantissa bits; 0..28 */
-    QMM_FP6_E2M3 = 3    /* 6-bit stream: sign, 2 exponent bits (bias 1), 3 mantissa bits; 0..7.5 */
+    QMM_FP6_E2M3 = 3,   /* 6-bit stream: sign, 2 exponent bits (bias 1), 3 mantissa bits; 0..7.5 */
+    /* 3-, 5- and 7-bit floats: no format in common use; of the bits after the sign, the
+       extra one goes to the exponent (the rule E2M1, E3M2 and E4M3 follow), bias
+       2^(e-1) - 1, subnormals at exponent 0, every code finite. */
+    QMM_FP3_E1M1 = 4,   /* 3-bit stream: sign, 1 exponent bit (bias 0), 1 mantissa bit; 0..3 */
+    QMM_FP5_E2M2 = 5,   /* 5-bit stream: sign, 2 exponent bits (bias 1), 2 mantissa bits; 0..7 */
+    QMM_FP7_E3M3 = 6    /* 7-bit stream: sign, 3 exponent bits (bias 3), 3 mantissa bits; 0..30 */
 };
 
 /* Y = X . W with W[k][n] = value(q[k][n]) * s[n][k / G] for floating-point codes
@@ -141,8 +212,11 @@ enum {
  * the values, fp32 accumulation, s applied per 128-row step in fp32);
  * otherwise the qmm_gemm kernel (one rounding multiply by s, then f16 MFMA
  * with fp32 accumulation).  wq is qmm_pack's stream of the code bit
- * patterns at 4 bits (E2M1), 6 bits (E3M2, E2M3) or 8 bits (E4M3); X, s, Y, M, K, N, G, stream and
- * the errors as for qmm_gemm; an unknown fmt gives QMM_ERR_INVALID_ARG. */
+ * patterns at 3 bits (E1M1), 4 bits (E2M1), 5 bits (E2M2), 6 bits (E3M2,
+ * E2M3), 7 bits (E3M3) or 8 bits (E4M3); the 3-, 5- and 7-bit codes are moved
+ * in registers into E2M1, E5M2 and E4M3 containers whose conversions, with a
+ * power-of-two scale, give the same exact values.  X, s, Y, M, K, N, G, stream
+ * and the errors as for qmm_gemm; an unknown fmt gives QMM_ERR_INVALID_ARG. */
 qmm_status qmm_gemm_fp(const qmm_half *X, const uint32_t *wq, const qmm_half *s, qmm_half *Y, int64_t M,
                        int64_t K, int64_t N, int fmt, int64_t G, qmm_stream stream);
 
@@ -200,6 +274,33 @@ const char *qmm_status_string(qmm_status status);
 
 /* Text of the last QMM_ERR_* reported on the calling host thread ("" if none). */
 const char *qmm_last_error(void);
+
+/* The same thread-local text under the name that reports HIP failures: after
+ * QMM_ERR_HIP it holds the entry point and hipGetErrorString() of the failed
+ * launch.  Alias of qmm_last_error(). */
+const char *qmm_last_hip_error(void);
+
+/* MEASUREMENT HOOKS.  Not part of the product: they compute nothing of Y and
+ * exist so that the kernels above can be priced against what this GPU
+ * delivers, beside the datasheet peaks (the Tilus verdict page, referee
+ * report: results against a stated reference point).  Both enqueue one
+ * kernel on stream and allocate nothing.
+ *
+ * qmm_probe_read: a plain streaming read of `bytes` bytes at device pointer
+ * buf (16-byte aligned, bytes a positive multiple of 16) by `grid`
+ * workgroups of 256 lanes, 16-byte non-temporal loads, 8 in flight per lane.
+ * sink: device uint32 [grid * 256], written only in the never-met case that
+ * the XOR of the data equals a fixed constant.
+ *
+ * qmm_probe_mfma: `iters` rounds of back-to-back f16 MFMAs with register
+ * operands in `grid` workgroups of 8 waves; shape 0 = v_mfma_f32_16x16x32_f16
+ * (8 accumulators per wave), shape 1 = v_mfma_f32_32x32x16_f16 (4 per wave).
+ * Work: grid * 8 * iters * 8 * 16384 flops for either shape.  sink: device
+ * float [grid * 512], written only in a never-met case.
+ * Errors: QMM_ERR_INVALID_ARG for null pointers, grid outside 1..65535,
+ * iters < 1, a bad size or shape. */
+qmm_status qmm_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, int grid, qmm_stream stream);
+qmm_status qmm_probe_mfma(float *sink, int iters, int grid, int shape, qmm_stream stream);
 
 #ifdef __cplusplus
 }
