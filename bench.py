@@ -155,6 +155,17 @@ def decode_launch(q, d):
     q.gemv(d["x"], wq, s, None, d["bits"], d["G"], out=d["y"])
 
 
+def grouped_launch(q, decs):
+    """The decode step as one qmm_gemv_grouped launch over the three products,
+    each reading its next rotating copy of the weights."""
+    probs = []
+    for d in decs:
+        wq, s = d["bufs"][d["i"] % len(d["bufs"])]
+        d["i"] += 1
+        probs.append((d["x"], wq, s, None, d["bits"]))
+    q.gemv_grouped(probs, decs[0]["G"], outs=[d["y"] for d in decs])
+
+
 def traffic_for(kernel_key):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
     committed rocprofv3 counter runs, or None unless those runs were taken on
@@ -501,6 +512,37 @@ def blas_context(torch, timer):
             "TFLOPs": round(tfs, 1), "frac_of_fp16_mfma_peak": round(tfs / FP16_MFMA_PEAK_TFS, 4)}
 
 
+def lut_leg(torch, q, synthetic, timer):
+    """1-bit codes on the 70B MLP-up shape at M = 1 (K 8192, N 28672, G 128,
+    per-group z): the table-lookup kernel (qmm_gemv_lut) beside the unpack
+    kernel (qmm_gemv), both streaming rotating weight copies from HBM."""
+    w = synthetic.BATCHED_70B
+    K, N, G = w["K"], w["N"], w["G"]
+    c = synthetic.make_case(1, K, N, 1, G, synthetic.seed_for(3, 1), per_group_z=True, s_range=w["s_range"])
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 1)
+    bufs = rotating(torch, (wq, torch.from_numpy(c["s"]).to("cuda:0"), torch.from_numpy(c["z"]).to("cuda:0")))
+    x = torch.from_numpy(c["X"]).to("cuda:0")
+    y = torch.empty((1, N), dtype=torch.float16, device="cuda:0")
+    alg = N * K // 8 + 2 * N * (K // G) * 2 + K * 2 + N * 2
+    out = {"workload": "70B MLP-up M1 K8192 N28672 k1 G128 per-group z"}
+    for name, fn in (("lut", q.gemv_lut), ("unpack", q.gemv)):
+        state = {"i": 0}
+
+        def launch(i, fn=fn, state=state):
+            b = bufs[state["i"] % len(bufs)]
+            state["i"] += 1
+            fn(x, b[0], b[1], b[2], 1, G, out=y)
+
+        for _ in range(3):
+            launch(0)
+        med, _ = timer.median_us(launch, per_region=10, regions=20)
+        out[name] = {"us_median": round(med, 2), "algorithmic_GBs": round(alg / med / 1e3, 1),
+                     "algorithmic_frac_of_hbm_peak": round(alg / med / 1e3 / HBM_PEAK_GBS, 4)}
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def gemm_leg(torch, q, synthetic, timer, reps):
     """The prefill product (M 2048, K = N = 4096, k 4, G 128) on the MFMA path.
     Cold: every launch reads its own copy of X, Wq and s out of a rotating set
@@ -573,12 +615,20 @@ def main():
             decode_launch(q, d)
     torch.cuda.synchronize()
 
-    # the step: three decode products (k = 3, 4, 6), back to back
+    # the step: the three decode products (k = 3, 4, 6) as one grouped launch
     print(f"bench: timing {args.steps} decode steps", file=sys.stderr, flush=True)
-    span = timer.region_ms(lambda i: [decode_launch(q, d) for d in decs], args.steps)
+    for _ in range(args.warmup):
+        grouped_launch(q, decs)
+    span = timer.region_ms(lambda i: grouped_launch(q, decs), args.steps)
     ms_per_step = span / args.steps
     wq_step = sum(d["wq_bytes"] for d in decs)
+    alg_step = sum(d["alg_bytes"] for d in decs)
     value = wq_step / (ms_per_step * 1e-3) / 1e9
+    step_median_us, _ = timer.median_us(lambda i: grouped_launch(q, decs), per_region=10, regions=50)
+    # the same products as three separate qmm_gemv launches, for comparison
+    sep = timer.region_ms(lambda i: [decode_launch(q, d) for d in decs], args.steps) / args.steps
+    separate = {"ms_per_step": round(sep, 5), "packed_GBs": round(wq_step / (sep * 1e-3) / 1e9, 1),
+                "packed_frac_of_peak": round(wq_step / (sep * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     # each kernel on its own: mean launch duration over the same number of
     # launches, and the median over 50 short regions
@@ -594,13 +644,13 @@ def main():
             "algorithmic_GBs": round(d["alg_bytes"] / (ms * 1e-3) / 1e9, 1),
             "packed_frac_of_peak": round(d["wq_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
-    dom = max(decs, key=lambda d: mean_ms[d["bits"]])
-    dom_ms = mean_ms[dom["bits"]]
-    achieved = dom["alg_bytes"] / (dom_ms * 1e-3) / 1e9
+    # the step's only kernel is the grouped one: its algorithmic bytes over its
+    # mean duration (one launch per step)
+    achieved = alg_step / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(f"gemv_m1_k{dom['bits']}"),
-                "kernel": f"qmm_gemv M=1 k={dom['bits']} (gemv_m1_kernel)",
-                "algorithmic_bytes_per_launch": dom["alg_bytes"]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for("gemv_grouped_7b"),
+                "kernel": "qmm_gemv_grouped k=3,4,6 (gemv_m1_grouped_kernel)",
+                "algorithmic_bytes_per_launch": alg_step}
     del decs
     torch.cuda.empty_cache()
 
@@ -631,9 +681,12 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": synthetic.DECODE_7B["name"] + " k{3,4,6}", "M": 1, "K": 4096, "N": 11008,
-                   "bits": [3, 4, 6], "G": 128, "launches_per_step": 3,
+                   "bits": [3, 4, 6], "G": 128, "launches_per_step": 1,
+                   "step": "the three products in one qmm_gemv_grouped launch",
                    "weights_read_from": "HBM (rotating copies > 1 GiB)"},
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "step_us_median_of_50": round(step_median_us, 3),
+        "separate_launches": separate,
         "roofline": roofline,
         "per_bits": per_bits,
         "gemm_m2048": gemm,
@@ -662,7 +715,8 @@ def run_suite(torch, q, synthetic, timer, reps):
             "prefill_fp7_e3m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 6),
             "decode_fp3_e1m1": decode_fp_suite(torch, q, synthetic, timer, reps, 4),
             "decode_fp5_e2m2": decode_fp_suite(torch, q, synthetic, timer, reps, 5),
-            "decode_fp7_e3m3": decode_fp_suite(torch, q, synthetic, timer, reps, 6)}
+            "decode_fp7_e3m3": decode_fp_suite(torch, q, synthetic, timer, reps, 6),
+            "lut_k1_70b": lut_leg(torch, q, synthetic, timer)}
 
 
 def run_only(args, torch, q, synthetic, timer, reps):
@@ -680,6 +734,12 @@ def run_only(args, torch, q, synthetic, timer, reps):
             out[f"k{bits}"] = {"us_per_launch": round(ms * 1e3, 3)}
             del d
             torch.cuda.empty_cache()
+    elif name == "grouped":
+        decs = [decode_setup(torch, q, synthetic, bits) for bits in synthetic.DECODE_7B["bits"]]
+        ms = timer.region_ms(lambda i: grouped_launch(q, decs), reps) / reps
+        out = {"step_us": round(ms * 1e3, 3)}
+    elif name == "lut":
+        out = lut_leg(torch, q, synthetic, timer)
     elif name == "gemm":
         out = gemm_leg(torch, q, synthetic, timer, reps)
     elif name == "batched":

@@ -27,20 +27,29 @@ template <int BITS>
 __device__ __forceinline__ void x_slots_e(const uint32_t (&xr)[16], half2_t (&xs)[16], int e)
 {
     using P = RunPlan<BITS>;
-    float x[32];
+    _Float16 x[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const half2_t p = as_half2(xr[i]);
-        x[2 * i] = (float)p[0];
-        x[2 * i + 1] = (float)p[1];
+        x[2 * i] = p[0];
+        x[2 * i + 1] = p[1];
     }
-    const float f = __builtin_ldexpf(1.0f, e);
+    // 2^(e - pos) as two fp16 powers of two: 2^a with a = clamp(e - pos, -14, 15),
+    // then 2^(e - pos - a), both exact (e <= 29, pos <= 10).  Each product is exact
+    // unless it leaves the fp16 normal range, which only activations below 2^-22 of
+    // the row maximum can do.
+    auto f1 = [&](int pos) { return (_Float16)__builtin_ldexpf(1.0f, min(15, max(-14, e - pos))); };
+    auto f2 = [&](int pos) { return (_Float16)__builtin_ldexpf(1.0f, e - pos - min(15, max(-14, e - pos))); };
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        half2_t v;
-        v[0] = (_Float16)(x[P::code[2 * j]] * (f * pow2neg(P::pos[2 * j])));
-        v[1] = (_Float16)(x[P::code[2 * j + 1]] * (f * pow2neg(P::pos[2 * j + 1])));
-        xs[j] = v;
+        half2_t v, a, b;
+        v[0] = x[P::code[2 * j]];
+        v[1] = x[P::code[2 * j + 1]];
+        a[0] = f1(P::pos[2 * j]);
+        a[1] = f1(P::pos[2 * j + 1]);
+        b[0] = f2(P::pos[2 * j]);
+        b[1] = f2(P::pos[2 * j + 1]);
+        xs[j] = (v * a) * b;
     }
 }
 
@@ -95,10 +104,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 }
 
 // e such that the row maximum |x| (given as its fp16 magnitude pattern) times
-// 2^e lies in [128, 256); 8 for an all-zero row (any value would do).
+// 2^e lies in [128, 256), at most 29 (a row whose largest value is an fp16
+// subnormal below 2^-21 stays below 128); 8 for an all-zero row (any value
+// would do).
 __device__ __forceinline__ int row_exponent(uint32_t maxbits)
 {
-    return 8 - __builtin_amdgcn_frexp_expf((float)as_half((uint16_t)maxbits));
+    return min(29, 8 - __builtin_amdgcn_frexp_expf((float)as_half((uint16_t)maxbits)));
 }
 
 // (1024 * 2^-pos + zc) for both halves of slot pair j: with h = 1024 + q 2^pos,
@@ -1089,8 +1100,11 @@ static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
 }
 
 // Grouped M = 1 products: the CUs are shared out in proportion to each
-// problem's estimated time (packed bytes plus a per-code compute share), at
-// least one workgroup each and enough that no wave takes more than 64 columns.
+// problem's estimated time, N (bits + 3): packed bytes plus a per-code share
+// for the unpack and dot products, which make the narrow codes relatively
+// costlier (on the 7B MLP shapes at k = 3, 4, 6 this split measured 15.7 us
+// against 17.5 us for a split by bytes alone); at least one workgroup each
+// and enough that no wave takes more than 64 columns.
 template <int RPL>
 static hipError_t grouped_go(const GroupArgs &ga, int grid, hipStream_t st)
 {
@@ -1111,7 +1125,7 @@ hipError_t launch_gemv_grouped(const GroupArgs &in, hipStream_t st)
     const int n = ga.count, cus = num_cus();
     double cost[QMM_GROUP_MAX], total = 0.0;
     for (int p = 0; p < n; ++p) {
-        cost[p] = (double)ga.p[p].N * ((double)ga.p[p].bits + 1.5);
+        cost[p] = (double)ga.p[p].N * ((double)ga.p[p].bits + 3.0);
         total += cost[p];
     }
     int nwg[QMM_GROUP_MAX], sum = 0, big = 0;

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256) void lut_m1_kernel(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                      uint16_t *__restrict__ Y, int K, int N, int G)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // static LDS (the kernel's only allocation, at address 0): table reads then
+    // need no base add, only the VGPR address and an immediate offset
+    __shared__ __attribute__((aligned(16))) uint8_t smem[16 * LUT_ROW + 4 * LUT_MAXR];
     float *T = reinterpret_cast<float *>(smem);                          // [16][8][256]
     float *xsum = reinterpret_cast<float *>(smem + 16 * LUT_ROW);        // [LUT_MAXR] per-run sums of x
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -176,20 +178,10 @@ static int lut_cus()
     return cus;
 }
 
-constexpr size_t LUT_LDS = 16 * LUT_ROW + 4 * LUT_MAXR;
-
 template <int RPL, int D, bool PGZ>
 static hipError_t lut_go(const GemvArgs &a, int grid, hipStream_t st)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&lut_m1_kernel<RPL, D, PGZ>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((lut_m1_kernel<RPL, D, PGZ>), dim3(grid), dim3(256), LUT_LDS, st, a.X, a.wq, a.s, a.z, a.Y, a.K, a.N,
-                       a.G);
+    hipLaunchKernelGGL((lut_m1_kernel<RPL, D, PGZ>), dim3(grid), dim3(256), 0, st, a.X, a.wq, a.s, a.z, a.Y, a.K, a.N, a.G);
     return hipGetLastError();
 }
 
