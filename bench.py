@@ -44,6 +44,10 @@ INT8_MFMA_PEAK_TOPS = 5033.2
 METRIC = "packed-weight HBM GB/s (% peak) at M=1; TFLOP/s (% MFMA peak) at M=2048"
 ROTATE_BYTES = 1 << 30
 PROFILE_TRAFFIC = os.path.join(HERE, "profiles", "traffic.json")
+PROFILE_VALU = os.path.join(HERE, "profiles", "valu.json")
+# VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 VALU instruction per
+# 4 cycles on a 16-lane SIMD = 614.4 G instructions/s = 39.3 T lane-ops/s
+VALU_PEAK_TLANEOPS = 256 * 4 * 2.4e9 / 4 * 64 / 1e12
 
 
 def parse():
@@ -66,6 +70,7 @@ def parse():
 # kernel only while these files are unchanged.
 KERNEL_SOURCES = {
     "gemv_m1": ("gemv.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
+    "lut": ("lut.hip", "qmm_device.hpp", "launch.hpp"),
     "gemm": ("gemm.hip", "qmm_device.hpp", "unpack_plan.inc", "launch.hpp"),
     "w4a8": ("w4a8.hip", "qmm_device.hpp", "launch.hpp"),
     "quantize": ("quantize.hip", "qmm_device.hpp", "launch.hpp"),
@@ -182,6 +187,35 @@ def traffic_for(kernel_key):
     if family not in KERNEL_SOURCES or e.get("source_digest") != source_digest(KERNEL_SOURCES[family]):
         return None
     return e.get("bytes_per_launch")
+
+
+def valu_for(kernel_key):
+    """VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, summed over the
+    GPU) from the committed counter run, or None unless it was taken on the
+    kernel's current sources."""
+    try:
+        with open(PROFILE_VALU) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get("kernels", {}).get(kernel_key)
+    if e is None:
+        return None
+    family = e.get("family")
+    if family not in KERNEL_SOURCES or e.get("source_digest") != source_digest(KERNEL_SOURCES[family]):
+        return None
+    return e.get("valu_insts_per_launch")
+
+
+def alu_roofline(kernel_key, us, codes):
+    """The plain-ALU roofline of a launch: VALU lane-ops per second against the
+    VALU issue peak, and lane-ops per weight code."""
+    insts = valu_for(kernel_key)
+    if insts is None:
+        return None
+    achieved = insts * 64 / (us * 1e-6) / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(VALU_PEAK_TLANEOPS, 2), "unit": "Tlane-op/s",
+            "frac": round(achieved / VALU_PEAK_TLANEOPS, 4), "valu_lane_ops_per_code": round(insts * 64 / codes, 3)}
 
 
 def cpu_model() -> str:
@@ -308,6 +342,8 @@ def batched_suite(torch, q, synthetic, timer, reps, only_bits=None, only_m=None)
             row[f"M{M}"] = {"us": round(ms * 1e3, 2), "packed_GBs": round(wq_bytes / ms / 1e6, 1),
                             "algorithmic_GBs": round(alg / ms / 1e6, 1),
                             "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            if bits <= 2:
+                row[f"M{M}"]["alu_roofline"] = alu_roofline(f"batched_70b_k{bits}_m{M}", ms * 1e3, K * N)
         out[f"k{bits}"] = row
         del bufs
         torch.cuda.empty_cache()
@@ -537,7 +573,8 @@ def lut_leg(torch, q, synthetic, timer):
             launch(0)
         med, _ = timer.median_us(launch, per_region=10, regions=20)
         out[name] = {"us_median": round(med, 2), "algorithmic_GBs": round(alg / med / 1e3, 1),
-                     "algorithmic_frac_of_hbm_peak": round(alg / med / 1e3 / HBM_PEAK_GBS, 4)}
+                     "algorithmic_frac_of_hbm_peak": round(alg / med / 1e3 / HBM_PEAK_GBS, 4),
+                     "alu_roofline": alu_roofline("lut_70b_k1" if name == "lut" else "batched_70b_k1_m1", med, K * N)}
     del bufs
     torch.cuda.empty_cache()
     return out
