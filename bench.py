@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--no-suite", action="store_true", help="skip the suite (batched decode, int8 activations, quantiser, float codes)")
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--only", default=None,
-                    help="run one leg and print its JSON (for profiling): decode, gemm, batched, w4a8, w8a8, "
+                    help="run one leg and print its JSON (for profiling): decode, grouped, gemm, batched, w4a8, w8a8, w4a8p, "
                          "quantize, fp, lut, probes")
     ap.add_argument("--bits", type=int, default=None, help="with --only: restrict to one code width")
     ap.add_argument("--M", type=int, default=None, help="with --only batched: restrict to one M")
@@ -382,6 +382,36 @@ def w4a8_suite(torch, q, synthetic, timer, reps, bits=4):
             "algorithmic_GBs": round(alg / ms / 1e6, 1),
             "algorithmic_frac_of_hbm_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
             "TOPs": round(2.0 * M * N * K / ms / 1e9, 2)}
+
+
+def w4a8_prefill_suite(torch, q, synthetic, timer, reps):
+    """W4A8 at prefill size (M 2048, K = N = 4096, k 4, G 128; the tiled i8-MFMA
+    kernel): TOPS against the dense int8 MFMA peak, Xq, Wq and s rotated."""
+    w = synthetic.PREFILL
+    M, K, N, G = w["M"], w["K"], w["N"], w["G"]
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(5, 4, 7), s_range=w["s_range"])
+    wq = q.pack(torch.from_numpy(c["codes"]).to("cuda:0"), 4)
+    bufs = rotating(torch, (torch.from_numpy(c["Xq"]).to("cuda:0"), wq, torch.from_numpy(c["s"]).to("cuda:0")))
+    del wq
+    sx = torch.from_numpy(c["sx"]).to("cuda:0")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    state = {"i": 0}
+
+    def launch(i):
+        b = bufs[state["i"] % len(bufs)]
+        state["i"] += 1
+        q.gemm_w4a8(b[0], sx, b[1], b[2], None, G, out=y)
+
+    for i in range(3):
+        launch(i)
+    ms = timer.region_ms(launch, reps) / reps
+    med, _ = timer.median_us(launch, 5, 50)
+    tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    del bufs
+    torch.cuda.empty_cache()
+    return {"workload": f"w4a8 prefill M{M} K{K} N{N} k4 G{G}", "cache": "cold (rotating Xq, Wq, s copies > 1 GiB)",
+            "us": round(ms * 1e3, 2), "us_median_of_50": round(med, 2), "TOPs": round(tops, 1),
+            "frac_of_int8_mfma_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4)}
 
 
 FP_NAMES = {0: "E2M1", 1: "E4M3", 2: "E3M2", 3: "E2M3", 4: "E1M1", 5: "E2M2", 6: "E3M3"}
@@ -740,6 +770,7 @@ def run_suite(torch, q, synthetic, timer, reps):
     return {"batched_decode_70b": batched_suite(torch, q, synthetic, timer, reps),
             "w4a8_8b": w4a8_suite(torch, q, synthetic, timer, reps),
             "w8a8_8b": w4a8_suite(torch, q, synthetic, timer, reps, bits=8),
+            "w4a8_prefill": w4a8_prefill_suite(torch, q, synthetic, timer, reps),
             "quantize_7b": quantize_suite(torch, q, synthetic, timer, reps),
             "prefill_fp4_e2m1": gemm_fp_suite(torch, q, synthetic, timer, reps, 0),
             "prefill_fp8_e4m3": gemm_fp_suite(torch, q, synthetic, timer, reps, 1),
@@ -783,6 +814,8 @@ def run_only(args, torch, q, synthetic, timer, reps):
         out = batched_suite(torch, q, synthetic, timer, reps, only_bits=args.bits, only_m=args.M)
     elif name in ("w4a8", "w8a8"):
         out = w4a8_suite(torch, q, synthetic, timer, reps, bits=4 if name == "w4a8" else 8)
+    elif name == "w4a8p":
+        out = w4a8_prefill_suite(torch, q, synthetic, timer, reps)
     elif name == "quantize":
         out = quantize_suite(torch, q, synthetic, timer, reps)
     elif name == "fp":

@@ -47,26 +47,7 @@ __device__ __forceinline__ void x_perm_g(const uint32_t (&xr)[16], half2_t (&xs)
 }
 
 constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
-constexpr int GEMM_GROUP_M = 4;          // M tiles per band of the tile order
 constexpr uint32_t GEMM_OOB = 0x80000000u;
-
-// Tile order: workgroup ids go round-robin over the 8 XCDs, so XCD x gets a
-// contiguous range of the tile sequence; the sequence walks bands of
-// GEMM_GROUP_M M tiles column tile by column tile, so the workgroups resident
-// on one XCD share both X row tiles and weight column tiles in its L2.
-__device__ __forceinline__ void gemm_tile(int mtiles, int ntiles, int &mt, int &nt)
-{
-    const int total = mtiles * ntiles;
-    int pid = blockIdx.x;
-    if (total % 8 == 0) pid = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
-    const int band = pid / (GEMM_GROUP_M * ntiles);
-    const int first = band * GEMM_GROUP_M;
-    const int rows = min(mtiles - first, GEMM_GROUP_M);
-    const int in_band = pid - band * GEMM_GROUP_M * ntiles;
-    mt = first + in_band % rows;
-    nt = in_band / rows;
-}
-
 // Workgroup tile BM (M) x 16 NS WV (N): WV waves side by side in N, each
 // BM x 16 NS = BM/16 x NS MFMA tiles, so every weight run is dequantised by
 // exactly one lane.  With 8 waves, two share each SIMD: one wave's
@@ -86,7 +67,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * GEMM_ROWB];
 
     int mt, nt;
-    gemm_tile(mtiles, ntiles, mt, nt);
+    band_tile(mtiles, ntiles, mt, nt);
     const int m0 = mt * BM, n0 = nt * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();

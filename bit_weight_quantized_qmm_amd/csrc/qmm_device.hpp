@@ -87,6 +87,25 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t o
 // built from it would be wrapped in a readfirstlane loop around every load.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Tile order of the prefill kernels: workgroup ids go round-robin over the 8
+// XCDs, so XCD x gets a contiguous range of the tile sequence; the sequence
+// walks bands of TILE_BAND_M M tiles column tile by column tile, so the
+// workgroups resident on one XCD share both X row tiles and weight column
+// tiles in its L2.
+constexpr int TILE_BAND_M = 4;
+__device__ __forceinline__ void band_tile(int mtiles, int ntiles, int &mt, int &nt)
+{
+    const int total = mtiles * ntiles;
+    int pid = blockIdx.x;
+    if (total % 8 == 0) pid = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+    const int band = pid / (TILE_BAND_M * ntiles);
+    const int first = band * TILE_BAND_M;
+    const int rows = min(mtiles - first, TILE_BAND_M);
+    const int in_band = pid - band * TILE_BAND_M * ntiles;
+    mt = first + in_band % rows;
+    nt = in_band / rows;
+}
+
 // fp32 sum over the 64 lanes of a wave; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float v)
 {

@@ -407,6 +407,257 @@ static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-sized products, k <= 7: the fp16 GEMM's tiling on the int8 MFMA.
+// Workgroup tile 128 (M) x 256 (N): 8 waves of 128 x 32 (8 x 2 MFMA tiles),
+// so every weight run is turned into int8 lanes by exactly one lane.  K step
+// 128 rows = 4 runs, lane group g owning run 4t + g; the step's X tile (in the
+// runs' byte order) and the s and z of the 256 columns are double-buffered in
+// LDS; X, s, z and the weight runs are loaded two steps ahead, into two
+// register sets that alternate with the step's parity.
+// B carries q - z itself: a run's int8 form plus 128 - z in every byte (no
+// carries, as q + 128 - z lies in 1..255 for q, z <= 127), sign bit flipped,
+// is q - z as a signed byte.  The MFMA sums over a group are then A of
+// BitLLM Sec. 4.4 directly, and the group's end applies y += s * float(A)
+// (the deferred dequantisation); Y = fp16(sx * y).
+// ---------------------------------------------------------------------------
+constexpr int WG_ROWB = 128 + 16;   // LDS bytes per X row (4 runs x 32 bytes + pad: conflict-free b128 reads)
+
+template <int BITS, int SPG, bool DUMP>
+__global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
+                                                        const uint32_t *__restrict__ wq, const uint16_t *__restrict__ s,
+                                                        const uint16_t *__restrict__ z, uint16_t *__restrict__ Y,
+                                                        int32_t *__restrict__ acc_out, int M, int K, int N, int G,
+                                                        int mtiles, int ntiles)
+{
+    static_assert(BITS >= 1 && BITS <= 7, "q - z must fit a signed byte");
+    constexpr int MS = 8, NS = 2;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * WG_ROWB];
+    __shared__ uint16_t ssz[2][2][256];   // [buffer][s, z][column of the tile], fp16 bits
+    int mt, nt;
+    band_tile(mtiles, ntiles, mt, nt);
+    const int m0 = mt * 128, n0 = nt * 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int R = K >> 5, ng = K / G;
+    const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
+    const int mrows = min(128, M - m0);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
+    const int wn0 = n0 + wave * 32;
+    const int wcols = max(0, min(32, N - wn0));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
+    // staging: thread t loads the 32 bytes of X row t / 4, run t % 4 of the
+    // step, and s (t < 256) or z (t >= 256) of tile column t % 256 (clamped:
+    // columns past N stage a valid column's values and are never written)
+    const int xrow = tid >> 2, xrun = tid & 3;
+    const bool stage_z = tid >= 256, zfill = stage_z && !z;   // zfill: stage the default z, 2^(k-1)
+    const uint16_t *szp = (stage_z && z ? z : s) + (size_t)min(n0 + (tid & 255), N - 1) * ng;
+    const uint16_t zdef = as_u16((_Float16)(float)(1 << (BITS - 1)));
+
+    struct XSet {
+        uint32_t x[8];
+        uint16_t sz;
+    };
+    auto load_x = [&](int tt, XSet &xs) {
+        const int run = 4 * tt + xrun;
+        const uint32_t off = run < R ? (uint32_t)xrow * (uint32_t)K + (uint32_t)run * 32u : W_OOB;
+        load_dwords<LOAD_DEFAULT>(xr, off, xs.x, 8);
+        xs.sz = szp[min((tt * 128) / G, ng - 1)];
+    };
+    auto store_x = [&](int buf, const XSet &xs) {
+        uint8_t *dst = &lds[buf][xrow * WG_ROWB + xrun * 32];
+        int4_t v0, v1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v0[e] = (int)wka8_xdword<BITS>(xs.x, e);
+            v1[e] = (int)wka8_xdword<BITS>(xs.x, 4 + e);
+        }
+        *reinterpret_cast<int4_t *>(dst) = v0;
+        *reinterpret_cast<int4_t *>(dst + 16) = v1;
+        ssz[buf][tid >> 8][tid & 255] = zfill ? zdef : xs.sz;
+    };
+    auto load_w = [&](int tt, uint32_t (&d)[NS][BITS]) {
+        const int run = 4 * tt + g;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            const uint32_t off = run < R ? (uint32_t)(ns * 16 + c) * col_bytes + (uint32_t)run * run_bytes : W_OOB;
+            load_dwords<LOAD_STREAM>(wr, off, d[ns], BITS);
+        }
+    };
+
+    float y[MS][NS][4];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[i][j][e] = 0.f;
+    int4_t acc[MS][NS];
+
+    XSet xa, xb;
+    uint32_t wa[NS][BITS], wb[NS][BITS];
+    load_x(0, xa);
+    load_w(0, wa);
+    store_x(0, xa);
+    load_x(1, xa);
+    load_w(1, wb);
+    load_x(2, xb);
+    __syncthreads();
+    const uint8_t *abase0 = &lds[0][c * WG_ROWB + g * 32];
+
+    // step tt: xin holds X(tt + 1), w the runs of step tt; afterwards they
+    // receive X(tt + 3) and the runs of step tt + 2.  sched_barriers keep the
+    // two steps of an iteration apart (their registers would otherwise be live
+    // together), and the empty asm statements keep everything computed from
+    // loaded values at its point of use (moved into the previous step, it
+    // would wait there for loads still in flight).
+    auto step = [&](int tt, bool first, XSet &xin, uint32_t (&w)[NS][BITS], float (&sc)[NS]) {
+        const int cur = tt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int b = 0; b < BITS; ++b) asm volatile("" : "+v"(w[ns][b]));
+        int4_t bv[NS][2];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            const int col = wave * 32 + ns * 16 + c;
+            const int zq = (int)(float)as_half(ssz[cur][1][col]);
+            const uint32_t cz = (uint32_t)(128 - zq) * 0x01010101u;
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[ns][v][e] = (int)((wka8_dword<BITS>(w[ns], 4 * v + e) + cz) ^ 0x80808080u);
+            if (first) sc[ns] = (float)as_half(ssz[cur][0][col]);
+        }
+        load_w(tt + 2, w);
+        const uint8_t *abase = abase0 + cur * (128 * WG_ROWB);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            int4_t a[MS];
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) a[ms] = *reinterpret_cast<const int4_t *>(abase + ms * 16 * WG_ROWB + v * 16);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const int4_t zero4 = {0, 0, 0, 0};
+                    acc[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ms], bv[ns][v],
+                                                                        (first && v == 0) ? zero4 : acc[ms][ns], 0, 0, 0);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(xin.x[q]));
+        asm volatile("" : "+v"(xin.sz));
+        store_x(cur ^ 1, xin);
+        load_x(tt + 3, xin);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto group_end = [&](int gi, const float (&sc)[NS]) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[ms][ns][i] = fmaf(sc[ns], (float)acc[ms][ns][i], y[ms][ns][i]);
+                    if constexpr (DUMP) {
+                        const int row = m0 + ms * 16 + 4 * g + i, col = wn0 + ns * 16 + c;
+                        if (row < M && col < N) acc_out[((size_t)row * ng + gi) * N + col] = acc[ms][ns][i];
+                    }
+                }
+    };
+    // a group of SPG steps; step tt uses register set A when tt is even
+    auto group = [&](int gi, bool odd) {
+        float sc[NS];
+#pragma unroll
+        for (int j = 0; j < SPG; ++j) {
+            if (((j & 1) != 0) == odd) step(gi * SPG + j, j == 0, xa, wa, sc);
+            else step(gi * SPG + j, j == 0, xb, wb, sc);
+        }
+        group_end(gi, sc);
+    };
+    if constexpr (SPG == 1) {
+        int gi = 0;
+        for (; gi + 1 < ng; gi += 2) {
+            group(gi, false);
+            group(gi + 1, true);
+        }
+        if (gi < ng) group(gi, false);
+    } else {
+        for (int gi = 0; gi < ng; ++gi) group(gi, false);
+    }
+
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + ms * 16 + 4 * g + i;
+            if (row >= M) continue;
+            const float sxm = (float)as_half(sx[row]);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                const int col = wn0 + ns * 16 + c;
+                if (col < N) Y[(size_t)row * N + col] = f32_to_f16_bits(sxm * y[ms][ns][i]);
+            }
+        }
+}
+
+template <int BITS, int SPG>
+static hipError_t w4a8_gemm_go(const W4A8Args &a, hipStream_t st)
+{
+    const int mtiles = (a.M + 127) / 128, ntiles = (a.N + 255) / 256;
+    const dim3 grid((unsigned)(mtiles * ntiles)), block(512);
+    if (a.acc)
+        hipLaunchKernelGGL((w4a8_gemm_kernel<BITS, SPG, true>), grid, block, 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y, a.acc,
+                           a.M, a.K, a.N, a.G, mtiles, ntiles);
+    else
+        hipLaunchKernelGGL((w4a8_gemm_kernel<BITS, SPG, false>), grid, block, 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y,
+                           a.acc, a.M, a.K, a.N, a.G, mtiles, ntiles);
+    return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t w4a8_gemm_launch(const W4A8Args &a, hipStream_t st)
+{
+    switch (a.G) {
+        case 128: return w4a8_gemm_go<BITS, 1>(a, st);
+        case 256: return w4a8_gemm_go<BITS, 2>(a, st);
+        case 512: return w4a8_gemm_go<BITS, 4>(a, st);
+        case 1024: return w4a8_gemm_go<BITS, 8>(a, st);
+        default: return hipErrorNotSupported;
+    }
+}
+
+static int w4a8_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        cus = (hipGetDevice(&dev) == hipSuccess &&
+               hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+    }
+    return cus;
+}
+
+// The tiled kernel when its estimated time is below the streaming kernel's.
+// Both estimates are measured on this GPU (K = 4096, k = 4): a workgroup of
+// the tiled kernel needs about 1.65 us per 128-row step, so a product takes
+// that times the K steps times the rounds of workgroups over the CUs; the
+// streaming kernel about 6.8e-9 us per multiply-add (it re-reads the weights
+// for every 16 rows).
+static bool w4a8_prefer_gemm(const W4A8Args &a)
+{
+    const long long tiles = (long long)((a.M + 127) / 128) * ((a.N + 255) / 256);
+    const long long cus = w4a8_cus();
+    const double rounds = (double)((tiles + cus - 1) / cus);
+    const double t_gemm = rounds * (a.K / 128) * 1.65;
+    const double t_stream = (double)a.M * a.N * a.K * 6.8e-9;
+    return t_gemm < t_stream;
+}
+
 template <int BITS, bool PGZ>
 static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipStream_t st)
 {
@@ -428,6 +679,9 @@ static hipError_t w4a8_go(const W4A8Args &a, int T, int passes, dim3 grid, hipSt
 template <int BITS>
 static hipError_t launch_wka8_bits(const W4A8Args &a, hipStream_t st)
 {
+    if constexpr (BITS <= 7) {
+        if (w4a8_prefer_gemm(a)) return w4a8_gemm_launch<BITS>(a, st);
+    }
     if (a.K <= 8192 && (size_t)a.N * (a.K / 32) * 4 * BITS < 0x7fffffffu) {
         const hipError_t e = a.z ? w4a8_stream_launch<BITS, true>(a, st) : w4a8_stream_launch<BITS, false>(a, st);
         if (e != hipErrorNotSupported) return e;

@@ -645,6 +645,57 @@ def test_wka8_many_tiles(q, orc, bits):
     check_wka8(orc, c, bits, Y, acc)
 
 
+# ------------------------------ int8 activations at prefill size (tiled) ---
+# Products whose M x N passes about 1.9 M (one round of 128 x 256 tiles costs
+# less than the streaming kernel's pass per 16 rows) take the tiled i8-MFMA
+# kernel for k <= 7; 1100 x 1800 is just past that, with ragged M and N tiles.
+GEMM8_M, GEMM8_N = 1100, 1800
+
+
+@pytest.mark.parametrize("bits", range(1, 8))
+@pytest.mark.parametrize("K,G,pgz", [(512, 128, False), (1024, 256, True), (1024, 512, False), (2048, 1024, True)])
+def test_wka8_gemm_shapes(q, orc, bits, K, G, pgz):
+    """The tiled int8 kernel: ragged M and N tiles, groups of 1, 2, 4 and 8 K
+    steps, the default and per-group zero-points; int32 group sums bit-exact."""
+    c = synthetic.make_w4a8_case(GEMM8_M, K, GEMM8_N, G, synthetic.seed_for(99, bits, K // G), bits=bits,
+                                 per_group_z=pgz)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+    Y2, _ = run_wka8(q, c, bits, with_acc=False)
+    assert torch.equal(Y.cpu(), Y2.cpu())
+
+
+@pytest.mark.parametrize("bits", [1, 4, 7])
+def test_wka8_gemm_extreme(q, orc, bits):
+    """-128 activations against the end codes, zero-points at both ends: the
+    byte-wise q - z of the tiled kernel at its extremes, sums exact."""
+    M, K, N, G = GEMM8_M, 512, GEMM8_N, 128
+    c = synthetic.make_w4a8_case(M, K, N, G, 40 + bits, bits=bits, per_group_z=True)
+    c["Xq"][::3] = -128
+    c["codes"][:, ::2] = (1 << bits) - 1
+    c["codes"][:, 1::2] = 0
+    c["z"][::2, :] = 0
+    c["z"][1::2, :] = (1 << bits) - 1
+    _, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], bits), c["s"], c["z"], G, bits=bits)
+    e = max(0, int(np.ceil(np.log2(np.abs(ref).max() / 16384.0))))
+    c["s"] = (c["s"].astype(np.float32) / (1 << e)).astype(np.float16)
+    Y, acc = run_wka8(q, c, bits)
+    check_wka8(orc, c, bits, Y, acc)
+
+
+def test_w4a8_prefill_workload(q, orc):
+    """W4A8 at prefill size (M 2048, K = N = 4096, k 4, G 128), the shape the
+    benchmark times: 16 whole rows of Y and of the int32 sums against the oracle."""
+    M, K, N, G = 2048, 4096, 4096, 128
+    c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(5, 4, 7))
+    Y, acc = run_w4a8(q, c)
+    rows = [128 * t + (53 * t) % 128 for t in range(16)]
+    A, ref = orc.w4a8(c["Xq"][rows], c["sx"][rows], orc.pack(c["codes"], 4), c["s"], None, G)
+    assert np.array_equal(acc[rows].cpu().numpy().astype(np.int64), A)
+    assert rel_err(Y[rows], ref) <= TOL
+    del acc
+
+
 # ---------------------------------------------------------- signed codes ---
 def signed_codes(bits, K, N, seed):
     g = synthetic.rng(seed)
