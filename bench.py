@@ -523,7 +523,7 @@ def probes_leg(torch, q, timer):
     out = {"read": {}, "mfma": {}}
     sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda:0")
     for name, nbytes in (("7B_k3_16.9MB", 16908288), ("7B_k4_22.5MB", 22544384), ("7B_k6_33.8MB", 33816576),
-                         ("1GiB", 1 << 30)):
+                         ("7B_step_73.3MB", 16908288 + 22544384 + 33816576), ("1GiB", 1 << 30)):
         best = None
         for wpc in (1, 2, 4, 8):
             grid = cus * wpc
@@ -727,6 +727,8 @@ def main():
     for k, r in per_bits.items():
         name = {"3": "7B_k3_16.9MB", "4": "7B_k4_22.5MB", "6": "7B_k6_33.8MB"}[k]
         r["frac_of_probe_read"] = round(r["packed_GBs"] / probes["read"][name]["GBs"], 4)
+    # the step against a plain streaming read of the same packed bytes
+    value_frac_of_probe = round(value / probes["read"]["7B_step_73.3MB"]["GBs"], 4)
 
     print("bench: timing the M=2048 prefill product", file=sys.stderr, flush=True)
     gemm = gemm_leg(torch, q, synthetic, timer, reps)
@@ -752,6 +754,7 @@ def main():
                    "step": "the three products in one qmm_gemv_grouped launch",
                    "weights_read_from": "HBM (rotating copies > 1 GiB)"},
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "value_frac_of_probe_read": value_frac_of_probe,
         "step_us_median_of_50": round(step_median_us, 3),
         "separate_launches": separate,
         "roofline": roofline,
