@@ -521,11 +521,11 @@ def probes_leg(torch, q, timer):
     big = torch.empty(3 << 28, dtype=torch.int32, device="cuda:0").fill_(7)   # 3 GiB, rotated through
     total = big.numel() * 4
     out = {"read": {}, "mfma": {}}
-    sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(cus * 16 * 256, dtype=torch.int32, device="cuda:0")
     for name, nbytes in (("7B_k3_16.9MB", 16908288), ("7B_k4_22.5MB", 22544384), ("7B_k6_33.8MB", 33816576),
                          ("7B_step_73.3MB", 16908288 + 22544384 + 33816576), ("1GiB", 1 << 30)):
         best = None
-        for wpc in (1, 2, 4, 8):
+        for wpc in (1, 2, 4, 8, 16):
             grid = cus * wpc
             nslices = max(2, total // nbytes - 1)
             state = {"i": 0}
