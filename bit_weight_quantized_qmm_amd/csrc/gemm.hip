@@ -54,17 +54,20 @@ constexpr uint32_t GEMM_OOB = 0x80000000u;
 // dequantisation and X staging run while the other's MFMAs issue (the wave's
 // accumulators, B fragments and one K slice of A fragments fit in half the
 // register file).
-template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM>
+template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM, int KP>
 __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
                                                    int ntiles)
 {
     using P = RunPlan<BITS>;
-    constexpr int BN = 16 * NS * WV;   // workgroup columns: WV waves of 16 NS columns
+    constexpr int CW = WV / KP;                               // waves side by side in N per K part
+    constexpr int BN = 16 * NS * CW;   // workgroup columns: CW waves of 16 NS columns
     constexpr int MS = BM / 16;                               // 16-row MFMA tiles per wave
-    constexpr int XP = (BM * 4 + 64 * WV - 1) / (64 * WV);   // (row, run) pieces of the X step per thread
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * GEMM_ROWB];
+    constexpr int XP = (BM * 4 + 64 * CW - 1) / (64 * CW);   // (row, run) pieces of the X step per thread
+    static_assert(WV % KP == 0, "whole waves per K part");
+    static_assert((KP - 1) * CW * MS * NS * 64 * 16 <= KP * 2 * BM * GEMM_ROWB, "partial sums fit the X tiles' LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[KP][2][BM * GEMM_ROWB];
 
     int mt, nt;
     band_tile(mtiles, ntiles, mt, nt);
@@ -73,6 +76,10 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G, TT = (R + 3) >> 2;
+    // K part kp of the workgroup's waves takes steps kp TS .. kp TS + TS - 1
+    // (past the last step every load is out of range and reads zeros)
+    const int kp = wave / CW, cw = wave - kp * CW, tp = tid - kp * 64 * CW;
+    const int TS = (TT + KP - 1) / KP, t0 = kp * TS;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const float zdef = (float)(1u << (BITS - 1));
 
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const int mrows = min(BM, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)((size_t)mrows * K * 2u));
     // Weights, scales, zero-points of this wave's 16 NS columns.
-    const int wn0 = n0 + wave * 16 * NS;
+    const int wn0 = n0 + cw * 16 * NS;
     const int wcols = max(0, min(16 * NS, N - wn0));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wq + (size_t)min(wn0, N) * R * BITS, (uint32_t)wcols * col_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(s + (size_t)min(wn0, N) * ng, (uint32_t)(wcols * ng * 2));
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     auto load_x = [&](int tt, uint32_t (&raw)[XP][16]) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
-            const int it = tid + 64 * WV * i;
+            const int it = tp + 64 * CW * i;
             const int row = it >> 2, gg = it & 3;
             const int run = 4 * tt + gg;
             const uint32_t off = (run < R && it < BM * 4) ? ((uint32_t)row * K + (uint32_t)run * 32u) * 2u : GEMM_OOB;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     auto store_x = [&](int buf, const uint32_t (&raw)[XP][16]) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
-            const int it = tid + 64 * WV * i;
+            const int it = tp + 64 * CW * i;
             if (it >= BM * 4) break;
             const int row = it >> 2, gg = it & 3;
             half2_t xs[16];
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
                 for (int j = 0; j < 16; ++j) xs[j] = as_half2(raw[i][j]);   // codes in order
             }
-            uint8_t *dst = &lds[buf][row * GEMM_ROWB + gg * 64];
+            uint8_t *dst = &lds[kp][buf][row * GEMM_ROWB + gg * 64];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 int4_t v;
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     uint32_t xraw[XP][16];
     uint32_t dcur[NS][BITS], dnext[NS][BITS];
     uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
-    load_x(0, xraw);
-    load_w(0, dcur, scur, zcur);
+    load_x(t0, xraw);
+    load_w(t0, dcur, scur, zcur);
     store_x(0, xraw);
     // Nothing stays in flight into the loop: the loop body then starts from the
     // same wait state on every iteration (the waits the compiler inserts for a
@@ -154,12 +161,12 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
-    const uint8_t *abase0 = &lds[0][c * GEMM_ROWB + g * 64];
-    for (int tt = 0; tt < TT; ++tt) {
+    const uint8_t *abase0 = &lds[kp][0][c * GEMM_ROWB + g * 64];
+    for (int tt = 0; tt < TS; ++tt) {
         const int cur = tt & 1;
-        // prefetch step tt + 1 (past the last step every load is out of range: zeros)
-        load_x(tt + 1, xraw);
-        load_w(tt + 1, dnext, snext, znext);
+        // prefetch the part's next step (past the last step every load is out of range: zeros)
+        load_x(t0 + tt + 1, xraw);
+        load_w(t0 + tt + 1, dnext, snext, znext);
         // dequantise this step's 4 runs (one per N subtile) into B fragments
         half8_t bq[NS][4];
 #pragma unroll
@@ -233,6 +240,28 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
         }
     }
 
+    // K parts: parts 1 .. KP - 1 leave their sums in LDS (over the X tiles), part
+    // 0 adds them in part order (a fixed order: the result does not depend on
+    // timing) and writes Y
+    if constexpr (KP > 1) {
+        float4_t *red = reinterpret_cast<float4_t *>(&lds[0][0][0]);
+        __syncthreads();
+        if (kp > 0) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) red[((((kp - 1) * CW + cw) * MS + ms) * NS + ns) * 64 + lane] = acc[ms][ns];
+        }
+        __syncthreads();
+        if (kp > 0) return;
+#pragma unroll
+        for (int q = 1; q < KP; ++q)
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) acc[ms][ns] += red[((((q - 1) * CW + cw) * MS + ms) * NS + ns) * 64 + lane];
+    }
+
     // epilogue: lane (g, c) of MFMA tile (ms, ns) holds rows 4g..4g+3, column c.
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -248,17 +277,17 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     }
 }
 
-template <int BITS, int FMT, int WV, int NS, int BM>
+template <int BITS, int FMT, int WV, int NS, int BM, int KP = 1>
 static hipError_t gemm_go(const GemvArgs &a, hipStream_t st)
 {
-    constexpr int BN = 16 * NS * WV;
+    constexpr int BN = 16 * NS * (WV / KP);
     const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
     const dim3 block(64 * WV), grid((unsigned)(mtiles * ntiles));
     if (FMT == 0 && a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     return hipGetLastError();
 }
@@ -274,20 +303,27 @@ static int gemm_cus()
     return cus;
 }
 
-// Tile choice: the first of 128 x 256 (8 waves of 32 columns), 128 x 128 and
-// 64 x 128 (8 waves of 16), 64 x 64 (4 waves of 16) whose grid gives every CU
-// a workgroup, else 64 x 64.  Each workgroup runs the whole K loop, so a grid
-// smaller than the CU count leaves the time of one workgroup's loop for a
-// fraction of the work; 8-wave tiles keep two waves per SIMD.
+// Tile choice.  Each workgroup walks its K range alone, so a grid with fewer
+// workgroups than CUs leaves the time of one workgroup's loop for a fraction
+// of the work; the candidates go from the largest tile to the smallest, and
+// the smaller ones split K among the workgroup's waves (K parts added in LDS
+// at the end): 128 x 256 (8 waves of 32 columns), 128 x 128 in 2 K parts,
+// 64 x 128 (8 waves of 16 columns), 64 x 64 in 2 parts, 64 x 32 in 4, and
+// 32 x 16 in 8 parts.  The first whose grid reaches 4/5 of the CUs is taken,
+// else the last.  Measured at K = 4096, k 4 (us): M 128: 23.7 -> 18.8;
+// M 256: 25.3 -> 23.6; M 1024: 59.2 -> 56.5; M 100, N 1000: 22.6 -> 12.5;
+// M 512 and M 2048 keep their tiles.
 template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
-    const long long cus = gemm_cus();
-    const long long m128 = (a.M + 127) / 128, m64 = (a.M + 63) / 64;
-    if (m128 * ((a.N + 255) / 256) >= cus) return gemm_go<BITS, FMT, 8, 2, 128>(a, st);
-    if (m128 * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1, 128>(a, st);
-    if (m64 * ((a.N + 127) / 128) >= cus) return gemm_go<BITS, FMT, 8, 1, 64>(a, st);
-    return gemm_go<BITS, FMT, 4, 1, 64>(a, st);
+    const long long cus = gemm_cus(), need = (4 * cus + 4) / 5;
+    auto tiles = [&](int bm, int bn) { return (long long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+    if (tiles(128, 256) >= need) return gemm_go<BITS, FMT, 8, 2, 128, 1>(a, st);
+    if (tiles(128, 128) >= need) return gemm_go<BITS, FMT, 8, 2, 128, 2>(a, st);
+    if (tiles(64, 128) >= need) return gemm_go<BITS, FMT, 8, 1, 64, 1>(a, st);
+    if (tiles(64, 64) >= need) return gemm_go<BITS, FMT, 8, 1, 64, 2>(a, st);
+    if (tiles(64, 32) >= need) return gemm_go<BITS, FMT, 8, 1, 64, 4>(a, st);
+    return gemm_go<BITS, FMT, 8, 1, 32, 8>(a, st);
 }
 
 hipError_t launch_gemm(const GemvArgs &a, hipStream_t st)

@@ -401,14 +401,17 @@ def test_batched_70b_workload(q, orc, bits):
         assert sampled_check(orc, Y, cm, seed=M, st=st) <= TOL, M
 
 
-@pytest.mark.parametrize("M,K,N,bits", [(2048, 256, 4096, 4), (1024, 512, 4056, 3), (512, 512, 4096, 5),
-                                         (500, 256, 4000, 8), (256, 512, 4096, 4), (130, 512, 300, 4),
-                                         (17, 1024, 2000, 6)])
+@pytest.mark.parametrize("M,K,N,bits", [(2048, 256, 4096, 4), (1024, 512, 4056, 3), (1000, 1152, 4000, 3),
+                                         (512, 512, 4096, 5), (500, 256, 4000, 8), (256, 512, 4096, 4),
+                                         (130, 512, 4000, 4), (130, 1152, 3000, 6), (130, 512, 300, 4),
+                                         (17, 1024, 2000, 6), (100, 1152, 1000, 7)])
 def test_gemm_tile_shapes(q, orc, M, K, N, bits):
     """Shapes that select each GEMM tile on a 256-CU part: 128 x 256 (M 2048),
-    128 x 128 (M 1024), 64 x 128 (M 500, 512), 64 x 64 (M 256 and the small
-    products), with ragged M and N edges; every tile computes each output with
-    the same MFMA sequence, so all are checked against the oracle in full."""
+    128 x 128 in 2 K parts (M 1000, 1024), 64 x 128 (M 500, 512), 64 x 64 in 2
+    parts (M 256), 64 x 32 in 4 parts (M 130, N 3000-4000), 32 x 16 in 8 parts
+    (the small products); ragged M and N edges, and K = 1152 (9 steps) so the
+    K parts are uneven and some get no step at all.  All checked against the
+    oracle in full."""
     c = synthetic.make_case(M, K, N, bits, 128, 560 + M + N + bits, per_group_z=(bits == 5))
     Y = run_product(q, q.gemm, c)
     ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, 128)
