@@ -82,6 +82,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const int TS = (TT + KP - 1) / KP, t0 = kp * TS;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const float zdef = (float)(1u << (BITS - 1));
+    const float ginv = run_group_inv(G);
 
     // X: rows m0.. of the whole K range (rows past M and runs past K read zeros).
     const int mrows = min(BM, M - m0);
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             const int col = ns * 16 + c;
             const uint32_t off = (run < R) ? (uint32_t)col * col_bytes + (uint32_t)run * run_bytes : GEMM_OOB;
             load_dwords<LOAD_STREAM>(wr, off, d[ns], BITS);
-            const uint32_t soff = (run < R) ? (uint32_t)(col * ng + (run * 32) / G) * 2u : GEMM_OOB;
+            const uint32_t soff = (run < R) ? (uint32_t)(col * ng + run_group(run, ginv)) * 2u : GEMM_OOB;
             sv[ns] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
             zv[ns] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, soff, 0, 0) : (uint16_t)0;
         }
@@ -167,6 +168,9 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
         // prefetch the part's next step (past the last step every load is out of range: zeros)
         load_x(t0 + tt + 1, xraw);
         load_w(t0 + tt + 1, dnext, snext, znext);
+        // issue the prefetch here: the scheduler would otherwise sink it to
+        // the end of the step, next to its first use
+        __builtin_amdgcn_sched_barrier(0);
         // dequantise this step's 4 runs (one per N subtile) into B fragments
         half8_t bq[NS][4];
 #pragma unroll

@@ -428,6 +428,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
+    const float ginv = run_group_inv(G);
     const uint32_t run_bytes = 4u * BITS;
     const uint32_t col_bytes = (uint32_t)R * run_bytes;
     const float zdef = (float)(1u << (BITS - 1));
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint16_t *__restri
                 const int run = 4 * (tt0 + t) + g;
                 const uint32_t off = (run < R) ? (uint32_t)c * col_bytes + (uint32_t)run * run_bytes : OOB;
                 load_dwords<LOAD_STREAM>(wr, off, d[t], BITS);
-                const uint32_t soff = (run < R) ? (uint32_t)(c * ng + (run * 32) / G) * 2u : OOB;
+                const uint32_t soff = (run < R) ? (uint32_t)(c * ng + run_group(run, ginv)) * 2u : OOB;
                 sv[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
                 zv[t] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, soff, 0, 0) : (uint16_t)0;
             }
@@ -544,6 +545,7 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using P = RunPlan<BITS>;
     const int R = K >> 5, R4 = (R + 3) & ~3, TT = R4 >> 2, ng = K / G;
+    const float ginv = run_group_inv(G);
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), nthreads = 64 * ks;
     const int g = lane >> 4, c = lane & 15;
     const int n0 = blockIdx.x * 16;
@@ -679,17 +681,17 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
             const float4_t cz = *reinterpret_cast<const float4_t *>(c2 + omc * R4 + 4 * tt);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int gi = min(((4 * tt + e) * 32) / G, ng - 1);
+                const int gi = min(run_group(4 * tt + e, ginv), ng - 1);
                 o.init[e] = -fmaf((float)as_half(zl[c * ng + gi]), cz[e], cb[e]);
                 o.sc[e] = (float)as_half(sl[c * ng + gi]);
             }
         } else {
             o.init = -cb;
             if (G128) {
-                o.sc[0] = (float)as_half(sl[c * ng + (tt * 128) / G]);
+                o.sc[0] = (float)as_half(sl[c * ng + run_group(4 * tt, ginv)]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o.sc[e] = (float)as_half(sl[c * ng + min(((4 * tt + e) * 32) / G, ng - 1)]);
+                for (int e = 0; e < 4; ++e) o.sc[e] = (float)as_half(sl[c * ng + min(run_group(4 * tt + e, ginv), ng - 1)]);
             }
         }
         if (PGZ && G128) o.sc[1] = o.sc[2] = o.sc[3] = o.sc[0];
@@ -787,6 +789,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
+    const float ginv = run_group_inv(G);
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int tiles = (N + 15) >> 4;
     const int tile0 = blockIdx.x * tpw;
@@ -920,7 +923,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
             for (int st = 0; st < S; ++st) {
                 const int slot = (jj * S + st) % D;
                 const int t = wave * S + st;
-                const uint32_t szv = sz[min((t * 128) / G, ng - 1) * SZW + 16 * j + c];
+                const uint32_t szv = sz[min(run_group(4 * t, ginv), ng - 1) * SZW + 16 * j + c];
                 uint32_t h[16];
                 if constexpr (FMT != 0) {
                     fp_run_to_half2<FMT>(d[slot], h);

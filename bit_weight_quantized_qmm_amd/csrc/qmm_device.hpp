@@ -87,6 +87,15 @@ __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t o
 // built from it would be wrapped in a readfirstlane loop around every load.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Index of the group that holds 32-code run r when a group spans gr runs
+// (gr = G / 32), i.e. r / gr, without an integer division (which costs about
+// 20 VALU instructions): inv = 1 / gr rounded to fp32, then
+// trunc((r + 1/2) inv).  (r + 1/2) / gr lies at least 1/(2 gr) from any
+// integer, and the two fp32 roundings move it by at most (r + 1/2) 2^-23 / gr,
+// less than that for r < 2^22 (run indices here stay below 2^16 + 8).
+__device__ __forceinline__ float run_group_inv(int G) { return 1.0f / (float)(G >> 5); }
+__device__ __forceinline__ int run_group(int r, float inv) { return (int)(((float)r + 0.5f) * inv); }
+
 // Tile order of the prefill kernels: workgroup ids go round-robin over the 8
 // XCDs, so XCD x gets a contiguous range of the tile sequence; the sequence
 // walks bands of TILE_BAND_M M tiles column tile by column tile, so the

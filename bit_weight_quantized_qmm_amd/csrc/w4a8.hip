@@ -103,6 +103,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
     const int g = lane >> 4, c = lane & 15;
     const int m0 = blockIdx.y * 16;
     const int R = K >> 5, ng = K / G, steps_per_group = G / 128;
+    const float ginv = run_group_inv(G);
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int mrows = min(16, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
                 const int run = 4 * tt + g;
                 const uint32_t off = (run < R) ? (uint32_t)c * col_bytes + (uint32_t)run * run_bytes : W_OOB;
                 load_dwords<LOAD_STREAM>(wr, off, d[t], BITS);
-                const uint32_t soff = (4 * tt < R) ? (uint32_t)(c * ng + (tt * 128) / G) * 2u : W_OOB;
+                const uint32_t soff = (4 * tt < R) ? (uint32_t)(c * ng + run_group(4 * tt, ginv)) * 2u : W_OOB;
                 sv[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
                 zv[t] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, soff, 0, 0) : (uint16_t)0;
             }
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(512) void w4a8_kernel(const int8_t *__restrict__ Xq
                 graw += raw;
                 gsx += sxg[t];
                 if ((tt + 1) % steps_per_group == 0 || 4 * (tt + 1) >= R) {
-                    const int grp = (tt * 128) / G;
+                    const int grp = run_group(4 * tt, ginv);
                     const int zz = wka8_zero<BITS, PGZ>(zv[t]);
                     const float sc = (float)as_half(sv[t]);
 #pragma unroll
@@ -440,6 +441,7 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int R = K >> 5, ng = K / G;
+    const float ginv = run_group_inv(G);
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int mrows = min(128, M - m0);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xq + (size_t)m0 * K, (uint32_t)((size_t)mrows * K));
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
         const int run = 4 * tt + xrun;
         const uint32_t off = run < R ? (uint32_t)xrow * (uint32_t)K + (uint32_t)run * 32u : W_OOB;
         load_dwords<LOAD_DEFAULT>(xr, off, xs.x, 8);
-        xs.sz = szp[min((tt * 128) / G, ng - 1)];
+        xs.sz = szp[min(run_group(4 * tt, ginv), ng - 1)];
     };
     auto store_x = [&](int buf, const XSet &xs) {
         uint8_t *dst = &lds[buf][xrow * WG_ROWB + xrun * 32];

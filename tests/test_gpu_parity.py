@@ -418,6 +418,20 @@ def test_gemm_tile_shapes(q, orc, M, K, N, bits):
     assert rel_err(Y, ref) <= TOL
 
 
+@pytest.mark.parametrize("bits", [1, 3, 4, 8])
+@pytest.mark.parametrize("M,fn", [(1, "gemv"), (5, "gemv"), (16, "gemv"), (130, "gemm"), (300, "gemm")])
+@pytest.mark.parametrize("K,G", [(480, 96), (1600, 160), (2240, 224), (3328, 416)])
+def test_group_sizes_not_power_of_two(q, orc, bits, M, fn, K, G):
+    """Groups of 3, 5, 7 and 13 runs of 32: the kernels find a run's group as
+    r / (G / 32) through a rounded reciprocal, which is inexact for these, and
+    the groups straddle the 128-row K steps."""
+    N = 70 if fn == "gemv" else 300
+    c = synthetic.make_case(M, K, N, bits, G, synthetic.seed_for(100, bits, M * 1000 + G), per_group_z=(bits != 4))
+    Y = run_product(q, getattr(q, fn), c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+    assert rel_err(Y, ref) <= TOL
+
+
 def test_prefill_workload(q, orc):
     """The prefill shape: 4000 sampled outputs, plus 16 whole rows (one in every
     128-row tile, at varying offsets inside the tile) against the oracle."""
