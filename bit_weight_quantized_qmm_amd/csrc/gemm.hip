@@ -9,9 +9,9 @@
 // unchanged), so both MFMA operands are plain 16-byte fragments.
 //
 // Workgroup tile 128 (M) x 256 (N), 8 waves side by side in N, wave tile
-// 128 x 32 = 8 x 2 MFMA tiles; products too small to give every CU a
-// workgroup that way take 128 x 128, 64 x 128 or 64 x 64 tiles (8, 8 or 4
-// waves of 16 columns).  K advances 128 rows per step: lane group g (lanes
+// 128 x 32 = 8 x 2 MFMA tiles; products with too few such tiles for the CUs
+// take smaller tiles whose waves also split K (2, 4 or 8 parts, summed in LDS
+// at the end).  K advances 128 rows per step: lane group g (lanes
 // 16g..16g+15) of every MFMA owns run 4t+g.
 //
 // Floating-point codes (FMT 1: E2M1 in 4-bit streams, FMT 2: E4M3 in 8-bit
@@ -46,7 +46,15 @@ __device__ __forceinline__ void x_perm_g(const uint32_t (&xr)[16], half2_t (&xs)
     }
 }
 
-constexpr int GEMM_ROWB = 4 * 64 + 16;   // LDS bytes per X row: 4 runs x 32 slots x fp16 + pad
+// X tile in LDS, per K step: run-major, [run g][row][four 16-byte chunks], the
+// chunk index XOR-ed with the run and with bits 2..3 of the row.  The 16 lanes
+// of an A-fragment read (rows c .. c + 15 of run g, chunk u) then spread over
+// 4 aligned 256-byte lines and over all 16 chunk slots mod 256 bytes, and so
+// do the 16 lanes of a staging write (rows r .. r + 3, runs 0..3): measured,
+// ds_read_b128 runs at twice the rate of the earlier row-major tile with a
+// 272-byte pitch.
+constexpr int GEMM_RUNB = 64;   // bytes of one (row, run): 32 codes' activations
+__device__ __forceinline__ int gemm_chunk(int row, int run, int q) { return 16 * (q ^ run ^ ((row >> 2) & 3)); }
 constexpr uint32_t GEMM_OOB = 0x80000000u;
 // Workgroup tile BM (M) x 16 NS WV (N): WV waves side by side in N, each
 // BM x 16 NS = BM/16 x NS MFMA tiles, so every weight run is dequantised by
@@ -66,8 +74,8 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     constexpr int MS = BM / 16;                               // 16-row MFMA tiles per wave
     constexpr int XP = (BM * 4 + 64 * CW - 1) / (64 * CW);   // (row, run) pieces of the X step per thread
     static_assert(WV % KP == 0, "whole waves per K part");
-    static_assert((KP - 1) * CW * MS * NS * 64 * 16 <= KP * 2 * BM * GEMM_ROWB, "partial sums fit the X tiles' LDS");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[KP][2][BM * GEMM_ROWB];
+    static_assert((KP - 1) * CW * MS * NS * 64 * 16 <= KP * 2 * BM * 4 * GEMM_RUNB, "partial sums fit the X tiles' LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[KP][2][BM * 4 * GEMM_RUNB];
 
     int mt, nt;
     band_tile(mtiles, ntiles, mt, nt);
@@ -95,7 +103,8 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     const __amdgpu_buffer_rsrc_t zr =
         make_rsrc(PGZ ? z + (size_t)min(wn0, N) * ng : s, PGZ ? (uint32_t)(wcols * ng * 2) : 0u);
 
-    // X staging: BM rows x 4 runs of 64 bytes per step, XP (row, run) pieces per thread.
+    // X staging: BM rows x 4 runs of 64 bytes per step, XP (row, run) pieces per
+    // thread, runs fastest (4 lanes load a row's 256 contiguous bytes).
     auto load_x = [&](int tt, uint32_t (&raw)[XP][16]) {
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
                 for (int j = 0; j < 16; ++j) xs[j] = as_half2(raw[i][j]);   // codes in order
             }
-            uint8_t *dst = &lds[kp][buf][row * GEMM_ROWB + gg * 64];
+            uint8_t *dst = &lds[kp][buf][(gg * BM + row) * GEMM_RUNB];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 int4_t v;
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
                 v[1] = (int)as_u32(xs[4 * q + 1]);
                 v[2] = (int)as_u32(xs[4 * q + 2]);
                 v[3] = (int)as_u32(xs[4 * q + 3]);
-                *reinterpret_cast<int4_t *>(dst + 16 * q) = v;
+                *reinterpret_cast<int4_t *>(dst + gemm_chunk(row, gg, q)) = v;
             }
         }
     };
@@ -162,7 +171,11 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
-    const uint8_t *abase0 = &lds[kp][0][c * GEMM_ROWB + g * 64];
+    // lane (g, c) reads rows c + 16 ms of run g; chunk u of a row lies at a
+    // row-dependent slot (the same for every ms: 16 ms leaves bits 2..3 alone)
+    const uint8_t *abase0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) abase0[u] = &lds[kp][0][(g * BM + c) * GEMM_RUNB + gemm_chunk(c, g, u)];
     for (int tt = 0; tt < TS; ++tt) {
         const int cur = tt & 1;
         // prefetch the part's next step (past the last step every load is out of range: zeros)
@@ -217,14 +230,15 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             }
           }
         }
-        const uint8_t *abase = abase0 + cur * (BM * GEMM_ROWB);
+        const int bufoff = cur * (BM * 4 * GEMM_RUNB);
         // per 32-row K slice u: the MS A fragments of the wave's BM rows, then
         // the slice's MFMAs over both column subtiles
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             half8_t a[MS];
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) a[ms] = *reinterpret_cast<const half8_t *>(abase + ms * 16 * GEMM_ROWB + u * 16);
+            for (int ms = 0; ms < MS; ++ms)
+                a[ms] = *reinterpret_cast<const half8_t *>(abase0[u] + bufoff + ms * 16 * GEMM_RUNB);
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
