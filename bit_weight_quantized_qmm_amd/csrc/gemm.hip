@@ -47,14 +47,15 @@ __device__ __forceinline__ void x_perm_g(const uint32_t (&xr)[16], half2_t (&xs)
 }
 
 // X tile in LDS, per K step: run-major, [run g][row][four 16-byte chunks], the
-// chunk index XOR-ed with the run and with bits 2..3 of the row.  The 16 lanes
-// of an A-fragment read (rows c .. c + 15 of run g, chunk u) then spread over
-// 4 aligned 256-byte lines and over all 16 chunk slots mod 256 bytes, and so
-// do the 16 lanes of a staging write (rows r .. r + 3, runs 0..3): measured,
-// ds_read_b128 runs at twice the rate of the earlier row-major tile with a
-// 272-byte pitch.
+// chunk index XOR-ed with 3g mod 4 and with bits 2..3 of the row.  Chosen by
+// measurement (the SQ_LDS_BANK_CONFLICT counter over a family of layouts): with
+// it neither the A-fragment reads (16 lanes: rows c .. c + 15 of run g, one
+// chunk) nor the staging writes (16 lanes: rows r .. r + 3, runs 0..3) wait on
+// bank conflicts, and ds_read_b128 runs at twice the rate of a row-major tile
+// with a 272-byte pitch; XOR-ing with g itself leaves the reads 2-way
+// conflicted.
 constexpr int GEMM_RUNB = 64;   // bytes of one (row, run): 32 codes' activations
-__device__ __forceinline__ int gemm_chunk(int row, int run, int q) { return 16 * (q ^ run ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int gemm_chunk(int row, int run, int q) { return 16 * (q ^ ((3 * run) & 3) ^ ((row >> 2) & 3)); }
 constexpr uint32_t GEMM_OOB = 0x80000000u;
 // Workgroup tile BM (M) x 16 NS WV (N): WV waves side by side in N, each
 // BM x 16 NS = BM/16 x NS MFMA tiles, so every weight run is dequantised by
@@ -62,7 +63,7 @@ constexpr uint32_t GEMM_OOB = 0x80000000u;
 // dequantisation and X staging run while the other's MFMAs issue (the wave's
 // accumulators, B fragments and one K slice of A fragments fit in half the
 // register file).
-template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM, int KP>
+template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM, int KP, int PIPE>
 __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
@@ -159,41 +160,17 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t xraw[XP][16];
-    uint32_t dcur[NS][BITS], dnext[NS][BITS];
-    uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
-    load_x(t0, xraw);
-    load_w(t0, dcur, scur, zcur);
-    store_x(0, xraw);
-    // Nothing stays in flight into the loop: the loop body then starts from the
-    // same wait state on every iteration (the waits the compiler inserts for a
-    // join of differently-pending paths would otherwise cover the prefetch).
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
-
-    // lane (g, c) reads rows c + 16 ms of run g; chunk u of a row lies at a
-    // row-dependent slot (the same for every ms: 16 ms leaves bits 2..3 alone)
-    const uint8_t *abase0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) abase0[u] = &lds[kp][0][(g * BM + c) * GEMM_RUNB + gemm_chunk(c, g, u)];
-    for (int tt = 0; tt < TS; ++tt) {
-        const int cur = tt & 1;
-        // prefetch the part's next step (past the last step every load is out of range: zeros)
-        load_x(t0 + tt + 1, xraw);
-        load_w(t0 + tt + 1, dnext, snext, znext);
-        // issue the prefetch here: the scheduler would otherwise sink it to
-        // the end of the step, next to its first use
-        __builtin_amdgcn_sched_barrier(0);
-        // dequantise this step's 4 runs (one per N subtile) into B fragments
-        half8_t bq[NS][4];
+    // dequantise a step's 4 runs (one per N subtile) into B fragments
+    auto dequant = [&](const uint32_t (&d)[NS][BITS], const uint16_t (&sv)[NS], const uint16_t (&zv)[NS],
+                       half8_t (&bq)[NS][4]) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
           if constexpr (FMT != 0) {
             half2_t s2;
-            s2[0] = as_half(scur[ns]);
+            s2[0] = as_half(sv[ns]);
             s2[1] = s2[0];
             uint32_t hf[16];
-            fp_run_to_half2<FMT>(dcur[ns], hf);
+            fp_run_to_half2<FMT>(d[ns], hf);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const half2_t w = as_half2(hf[j]) * s2;   // exact value, one rounding
@@ -202,12 +179,12 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             }
           } else {
             uint32_t h[16];
-            run_to_half2<BITS>(dcur[ns], h);
+            run_to_half2<BITS>(d[ns], h);
             half2_t s2;
-            s2[0] = as_half(scur[ns]);
+            s2[0] = as_half(sv[ns]);
             s2[1] = s2[0];
             half2_t z2;
-            z2[0] = as_half(zcur[ns]);
+            z2[0] = as_half(zv[ns]);
             z2[1] = z2[0];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -230,9 +207,16 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
             }
           }
         }
+    };
+    // lane (g, c) reads rows c + 16 ms of run g; chunk u of a row lies at a
+    // row-dependent slot (the same for every ms: 16 ms leaves bits 2..3 alone)
+    const uint8_t *abase0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) abase0[u] = &lds[kp][0][(g * BM + c) * GEMM_RUNB + gemm_chunk(c, g, u)];
+    // per 32-row K slice u: the MS A fragments of the wave's BM rows, then the
+    // slice's MFMAs over the column subtiles
+    auto mfmas = [&](int cur, const half8_t (&bq)[NS][4]) {
         const int bufoff = cur * (BM * 4 * GEMM_RUNB);
-        // per 32-row K slice u: the MS A fragments of the wave's BM rows, then
-        // the slice's MFMAs over both column subtiles
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             half8_t a[MS];
@@ -242,19 +226,116 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
+                for (int ms = 0; ms < MS; ++ms) {
                     acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
+                    if constexpr (PIPE == 2 && FMT == 0) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // then two VALU
+                    }
+                }
         }
-        // the X permutation waits for this step's prefetch: keep it after the MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-        store_x(cur ^ 1, xraw);
+    };
+
+    uint32_t xraw[XP][16];
+    if constexpr (PIPE == 0) {
+        uint32_t dcur[NS][BITS], dnext[NS][BITS];
+        uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
+        load_x(t0, xraw);
+        load_w(t0, dcur, scur, zcur);
+        store_x(0, xraw);
+        // Nothing stays in flight into the loop: the loop body then starts from the
+        // same wait state on every iteration (the waits the compiler inserts for a
+        // join of differently-pending paths would otherwise cover the prefetch).
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         __syncthreads();
+        for (int tt = 0; tt < TS; ++tt) {
+            const int cur = tt & 1;
+            // prefetch the part's next step (past the last step every load is out of range: zeros)
+            load_x(t0 + tt + 1, xraw);
+            load_w(t0 + tt + 1, dnext, snext, znext);
+            // issue the prefetch here: the scheduler would otherwise sink it to
+            // the end of the step, next to its first use
+            __builtin_amdgcn_sched_barrier(0);
+            half8_t bq[NS][4];
+            dequant(dcur, scur, zcur, bq);
+            mfmas(cur, bq);
+            // the X permutation waits for this step's prefetch: keep it after the MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(cur ^ 1, xraw);
+            __syncthreads();
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
+            for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
-            for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
-            scur[ns] = snext[ns];
-            zcur[ns] = znext[ns];
+                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
+                scur[ns] = snext[ns];
+                zcur[ns] = znext[ns];
+            }
+        }
+    } else if constexpr (PIPE == 3) {
+        // X loaded two steps ahead (two register sets, roles alternating with
+        // the step's parity)
+        uint32_t xB[XP][16];
+        uint32_t dcur[NS][BITS], dnext[NS][BITS];
+        uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
+        load_x(t0, xraw);
+        load_w(t0, dcur, scur, zcur);
+        store_x(0, xraw);
+        load_x(t0 + 1, xB);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        __syncthreads();
+        auto step = [&](int tt, uint32_t (&xl)[XP][16], const uint32_t (&xs)[XP][16]) {
+            const int cur = tt & 1;
+            load_x(t0 + tt + 2, xl);
+            load_w(t0 + tt + 1, dnext, snext, znext);
+            __builtin_amdgcn_sched_barrier(0);
+            half8_t bq[NS][4];
+            dequant(dcur, scur, zcur, bq);
+            mfmas(cur, bq);
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(cur ^ 1, xs);
+            __syncthreads();
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+#pragma unroll
+                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
+                scur[ns] = snext[ns];
+                zcur[ns] = znext[ns];
+            }
+        };
+        for (int tt = 0; tt < TS; tt += 2) {
+            step(tt, xraw, xB);
+            if (tt + 1 < TS) step(tt + 1, xB, xraw);
+        }
+    } else {
+        // B of step t + 1 is dequantised during step t's MFMAs: two B sets and
+        // two sets of raw runs (loaded two steps ahead), roles alternating with
+        // the step's parity
+        half8_t bA[NS][4], bB[NS][4];
+        uint32_t dA[NS][BITS], dB[NS][BITS];
+        uint16_t sA[NS], sB[NS], zA[NS], zB[NS];
+        load_x(t0, xraw);
+        load_w(t0, dA, sA, zA);
+        load_w(t0 + 1, dB, sB, zB);
+        store_x(0, xraw);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        dequant(dA, sA, zA, bA);
+        __syncthreads();
+        auto step = [&](int tt, const half8_t (&bc)[NS][4], half8_t (&bn)[NS][4], uint32_t (&dc)[NS][BITS],
+                        uint16_t (&sc)[NS], uint16_t (&zc)[NS], const uint32_t (&dn)[NS][BITS], const uint16_t (&sn)[NS],
+                        const uint16_t (&zn)[NS]) {
+            const int cur = tt & 1;
+            load_x(t0 + tt + 1, xraw);
+            load_w(t0 + tt + 2, dc, sc, zc);   // step tt's runs are in bc already
+            __builtin_amdgcn_sched_barrier(0);
+            dequant(dn, sn, zn, bn);           // step tt + 1, loaded a step ago
+            mfmas(cur, bc);
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(cur ^ 1, xraw);
+            __syncthreads();
+        };
+        for (int tt = 0; tt < TS; tt += 2) {
+            step(tt, bA, bB, dA, sA, zA, dB, sB, zB);
+            if (tt + 1 < TS) step(tt + 1, bB, bA, dB, sB, zB, dA, sA, zA);
         }
     }
 
@@ -295,17 +376,17 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     }
 }
 
-template <int BITS, int FMT, int WV, int NS, int BM, int KP = 1>
+template <int BITS, int FMT, int WV, int NS, int BM, int KP = 1, int PIPE = 0>
 static hipError_t gemm_go(const GemvArgs &a, hipStream_t st)
 {
     constexpr int BN = 16 * NS * (WV / KP);
     const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
     const dim3 block(64 * WV), grid((unsigned)(mtiles * ntiles));
     if (FMT == 0 && a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM, KP, PIPE>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM, KP, PIPE>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     return hipGetLastError();
 }
