@@ -63,7 +63,7 @@ constexpr uint32_t GEMM_OOB = 0x80000000u;
 // dequantisation and X staging run while the other's MFMAs issue (the wave's
 // accumulators, B fragments and one K slice of A fragments fit in half the
 // register file).
-template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM, int KP, int PIPE>
+template <int BITS, bool PGZ, int FMT, int WV, int NS, int BM, int KP>
 __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                    const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                    uint16_t *__restrict__ Y, int M, int K, int N, int G, int mtiles,
@@ -228,117 +228,44 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], bq[ns][u], acc[ms][ns], 0, 0, 0);
-                    if constexpr (PIPE == 2 && FMT == 0) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // then two VALU
-                    }
                 }
         }
     };
 
     uint32_t xraw[XP][16];
-    if constexpr (PIPE == 0) {
-        uint32_t dcur[NS][BITS], dnext[NS][BITS];
-        uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
-        load_x(t0, xraw);
-        load_w(t0, dcur, scur, zcur);
-        store_x(0, xraw);
-        // Nothing stays in flight into the loop: the loop body then starts from the
-        // same wait state on every iteration (the waits the compiler inserts for a
-        // join of differently-pending paths would otherwise cover the prefetch).
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    uint32_t dcur[NS][BITS], dnext[NS][BITS];
+    uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
+    load_x(t0, xraw);
+    load_w(t0, dcur, scur, zcur);
+    store_x(0, xraw);
+    // Nothing stays in flight into the loop: the loop body then starts from the
+    // same wait state on every iteration (the waits the compiler inserts for a
+    // join of differently-pending paths would otherwise cover the prefetch).
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    for (int tt = 0; tt < TS; ++tt) {
+        const int cur = tt & 1;
+        // prefetch the part's next step (past the last step every load is out of range: zeros)
+        load_x(t0 + tt + 1, xraw);
+        load_w(t0 + tt + 1, dnext, snext, znext);
+        // issue the prefetch here: the scheduler would otherwise sink it to
+        // the end of the step, next to its first use
+        __builtin_amdgcn_sched_barrier(0);
+        half8_t bq[NS][4];
+        dequant(dcur, scur, zcur, bq);
+        mfmas(cur, bq);
+        // the X permutation waits for this step's prefetch: keep it after the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(cur ^ 1, xraw);
         __syncthreads();
-        for (int tt = 0; tt < TS; ++tt) {
-            const int cur = tt & 1;
-            // prefetch the part's next step (past the last step every load is out of range: zeros)
-            load_x(t0 + tt + 1, xraw);
-            load_w(t0 + tt + 1, dnext, snext, znext);
-            // issue the prefetch here: the scheduler would otherwise sink it to
-            // the end of the step, next to its first use
-            __builtin_amdgcn_sched_barrier(0);
-            half8_t bq[NS][4];
-            dequant(dcur, scur, zcur, bq);
-            mfmas(cur, bq);
-            // the X permutation waits for this step's prefetch: keep it after the MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            store_x(cur ^ 1, xraw);
-            __syncthreads();
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
-                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
-                scur[ns] = snext[ns];
-                zcur[ns] = znext[ns];
-            }
-        }
-    } else if constexpr (PIPE == 3) {
-        // X loaded two steps ahead (two register sets, roles alternating with
-        // the step's parity)
-        uint32_t xB[XP][16];
-        uint32_t dcur[NS][BITS], dnext[NS][BITS];
-        uint16_t scur[NS], snext[NS], zcur[NS], znext[NS];
-        load_x(t0, xraw);
-        load_w(t0, dcur, scur, zcur);
-        store_x(0, xraw);
-        load_x(t0 + 1, xB);
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-        __syncthreads();
-        auto step = [&](int tt, uint32_t (&xl)[XP][16], const uint32_t (&xs)[XP][16]) {
-            const int cur = tt & 1;
-            load_x(t0 + tt + 2, xl);
-            load_w(t0 + tt + 1, dnext, snext, znext);
-            __builtin_amdgcn_sched_barrier(0);
-            half8_t bq[NS][4];
-            dequant(dcur, scur, zcur, bq);
-            mfmas(cur, bq);
-            __builtin_amdgcn_sched_barrier(0);
-            store_x(cur ^ 1, xs);
-            __syncthreads();
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-#pragma unroll
-                for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
-                scur[ns] = snext[ns];
-                zcur[ns] = znext[ns];
-            }
-        };
-        for (int tt = 0; tt < TS; tt += 2) {
-            step(tt, xraw, xB);
-            if (tt + 1 < TS) step(tt + 1, xB, xraw);
-        }
-    } else {
-        // B of step t + 1 is dequantised during step t's MFMAs: two B sets and
-        // two sets of raw runs (loaded two steps ahead), roles alternating with
-        // the step's parity
-        half8_t bA[NS][4], bB[NS][4];
-        uint32_t dA[NS][BITS], dB[NS][BITS];
-        uint16_t sA[NS], sB[NS], zA[NS], zB[NS];
-        load_x(t0, xraw);
-        load_w(t0, dA, sA, zA);
-        load_w(t0 + 1, dB, sB, zB);
-        store_x(0, xraw);
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-        dequant(dA, sA, zA, bA);
-        __syncthreads();
-        auto step = [&](int tt, const half8_t (&bc)[NS][4], half8_t (&bn)[NS][4], uint32_t (&dc)[NS][BITS],
-                        uint16_t (&sc)[NS], uint16_t (&zc)[NS], const uint32_t (&dn)[NS][BITS], const uint16_t (&sn)[NS],
-                        const uint16_t (&zn)[NS]) {
-            const int cur = tt & 1;
-            load_x(t0 + tt + 1, xraw);
-            load_w(t0 + tt + 2, dc, sc, zc);   // step tt's runs are in bc already
-            __builtin_amdgcn_sched_barrier(0);
-            dequant(dn, sn, zn, bn);           // step tt + 1, loaded a step ago
-            mfmas(cur, bc);
-            __builtin_amdgcn_sched_barrier(0);
-            store_x(cur ^ 1, xraw);
-            __syncthreads();
-        };
-        for (int tt = 0; tt < TS; tt += 2) {
-            step(tt, bA, bB, dA, sA, zA, dB, sB, zB);
-            if (tt + 1 < TS) step(tt + 1, bB, bA, dB, sB, zB, dA, sA, zA);
+            for (int b = 0; b < BITS; ++b) dcur[ns][b] = dnext[ns][b];
+            scur[ns] = snext[ns];
+            zcur[ns] = znext[ns];
         }
     }
-
     // K parts: parts 1 .. KP - 1 leave their sums in LDS (over the X tiles), part
     // 0 adds them in part order (a fixed order: the result does not depend on
     // timing) and writes Y
@@ -376,17 +303,17 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const uint16_t *__restric
     }
 }
 
-template <int BITS, int FMT, int WV, int NS, int BM, int KP = 1, int PIPE = 0>
+template <int BITS, int FMT, int WV, int NS, int BM, int KP = 1>
 static hipError_t gemm_go(const GemvArgs &a, hipStream_t st)
 {
     constexpr int BN = 16 * NS * (WV / KP);
     const int mtiles = (a.M + BM - 1) / BM, ntiles = (a.N + BN - 1) / BN;
     const dim3 block(64 * WV), grid((unsigned)(mtiles * ntiles));
     if (FMT == 0 && a.z)
-        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM, KP, PIPE>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, true, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM, KP, PIPE>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
+        hipLaunchKernelGGL((gemm_kernel<BITS, false, FMT, WV, NS, BM, KP>), grid, block, 0, st, a.X, a.wq, a.s, a.z, a.Y, a.M,
                            a.K, a.N, a.G, mtiles, ntiles);
     return hipGetLastError();
 }
