@@ -422,7 +422,16 @@ static hipError_t w4a8_stream_launch(const W4A8Args &a, hipStream_t st)
 // BitLLM Sec. 4.4 directly, and the group's end applies y += s * float(A)
 // (the deferred dequantisation); Y = fp16(sx * y).
 // ---------------------------------------------------------------------------
-constexpr int WG_ROWB = 128 + 16;   // LDS bytes per X row (4 runs x 32 bytes + pad: conflict-free b128 reads)
+// X tile in LDS, per K step: run-major, [run g][row][two 16-byte chunks],
+// rows XOR-ed with g and the chunk index with bit 2 of the row and bit 0 of
+// g.  Chosen by measurement (the SQ_LDS_BANK_CONFLICT counter over a family
+// of layouts): neither the A-fragment reads nor the staging writes wait on
+// bank conflicts; a row-major tile with a 144-byte pitch conflicts on both.
+constexpr int WG_RUNB = 128 * 32;   // bytes of one run's column of the tile
+__device__ __forceinline__ int wg_xoff(int row, int run, int q)
+{
+    return run * WG_RUNB + 32 * (row ^ run) + 16 * (q ^ ((row >> 2) & 1) ^ (run & 1));
+}
 
 template <int BITS, int SPG, bool DUMP>
 __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict__ Xq, const uint16_t *__restrict__ sx,
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
 {
     static_assert(BITS >= 1 && BITS <= 7, "q - z must fit a signed byte");
     constexpr int MS = 8, NS = 2;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * WG_ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * WG_RUNB];
     __shared__ uint16_t ssz[2][2][256];   // [buffer][s, z][column of the tile], fp16 bits
     int mt, nt;
     band_tile(mtiles, ntiles, mt, nt);
@@ -467,15 +476,15 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
         xs.sz = szp[min(run_group(4 * tt, ginv), ng - 1)];
     };
     auto store_x = [&](int buf, const XSet &xs) {
-        uint8_t *dst = &lds[buf][xrow * WG_ROWB + xrun * 32];
+        uint8_t *dst = &lds[buf][0];
         int4_t v0, v1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             v0[e] = (int)wka8_xdword<BITS>(xs.x, e);
             v1[e] = (int)wka8_xdword<BITS>(xs.x, 4 + e);
         }
-        *reinterpret_cast<int4_t *>(dst) = v0;
-        *reinterpret_cast<int4_t *>(dst + 16) = v1;
+        *reinterpret_cast<int4_t *>(dst + wg_xoff(xrow, xrun, 0)) = v0;
+        *reinterpret_cast<int4_t *>(dst + wg_xoff(xrow, xrun, 1)) = v1;
         ssz[buf][tid >> 8][tid & 255] = zfill ? zdef : xs.sz;
     };
     auto load_w = [&](int tt, uint32_t (&d)[NS][BITS]) {
@@ -505,7 +514,8 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
     load_w(1, wb);
     load_x(2, xb);
     __syncthreads();
-    const uint8_t *abase0 = &lds[0][c * WG_ROWB + g * 32];
+    // lane (g, c) reads rows c + 16 ms of run g (16 ms leaves the XOR terms alone)
+    const uint8_t *abase0[2] = {&lds[0][wg_xoff(c, g, 0)], &lds[0][wg_xoff(c, g, 1)]};
 
     // step tt: xin holds X(tt + 1), w the runs of step tt; afterwards they
     // receive X(tt + 3) and the runs of step tt + 2.  sched_barriers keep the
@@ -533,12 +543,12 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
             if (first) sc[ns] = (float)as_half(ssz[cur][0][col]);
         }
         load_w(tt + 2, w);
-        const uint8_t *abase = abase0 + cur * (128 * WG_ROWB);
+        const int bufoff = cur * (4 * WG_RUNB);
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
             int4_t a[MS];
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) a[ms] = *reinterpret_cast<const int4_t *>(abase + ms * 16 * WG_ROWB + v * 16);
+            for (int ms = 0; ms < MS; ++ms) a[ms] = *reinterpret_cast<const int4_t *>(abase0[v] + bufoff + ms * 16 * 32);
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
