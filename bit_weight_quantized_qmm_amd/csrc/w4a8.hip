@@ -19,6 +19,7 @@
 // rows = 4 runs, lane group g owning run 4t+g.  Requires G % 128 == 0 so that
 // every K step lies inside one group.
 #include <algorithm>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "qmm_device.hpp"
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
     const int m0 = blockIdx.y * 16;
     const int mrows = min(16, M - m0);
     const int R = K >> 5, ng = K / G, TT = R >> 2, sp = G >> 7;
+    const bool dump = acc_out != nullptr;
     const uint32_t run_bytes = 4u * BITS, col_bytes = (uint32_t)R * run_bytes;
     const int tiles = (N + 15) >> 4;
     const int tile0 = blockIdx.x * tpw;
@@ -300,50 +302,67 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
 
     // UT tiles per loop iteration keep every ring slot a compile-time index
     constexpr int UT = D > S ? D / S : 1;
+    // the tile loop, compiled twice: SP1 (G = 128, every step ends its group:
+    // no running sums) and the general case; a uniform branch picks one
+    const int lsp = __builtin_ctz((unsigned)sp);   // sp = G / 128 is a power of two
+    auto tiles_loop = [&](auto sp1_tag) {
+        constexpr bool SP1 = decltype(sp1_tag)::value;
 #pragma unroll 1
-    for (int jb = 0; jb < ntile; jb += UT) {
+        for (int jb = 0; jb < ntile; jb += UT) {
 #pragma unroll
-        for (int jj = 0; jj < UT; ++jj) {
-            const int j = jb + jj;
-            float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
-            int4_t graw = {0, 0, 0, 0}, gsx = {0, 0, 0, 0};
-            const int n = 16 * (tile0 + j) + c;
+            for (int jj = 0; jj < UT; ++jj) {
+                const int j = jb + jj;
+                float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
+                int4_t graw = {0, 0, 0, 0}, gsx = {0, 0, 0, 0};
+                const int n = 16 * (tile0 + j) + c;
 #pragma unroll
-            for (int st = 0; st < S; ++st) {
-                const int slot = (jj * S + st) % D;
-                const int t = wave * S + st;
-                const uint32_t szv = sz[min(t / sp, ng - 1) * SZW + 16 * j + c];
-                int4_t raw = {0, 0, 0, 0};
+                for (int st = 0; st < S; ++st) {
+                    const int slot = (jj * S + st) % D;
+                    const int t = wave * S + st;
+                    const int grp = SP1 ? t : t >> lsp;
+                    const uint32_t szv = sz[min(grp, ng - 1) * SZW + 16 * j + c];
+                    int4_t raw = {0, 0, 0, 0};
 #pragma unroll
-                for (int v = 0; v < 2; ++v) {
-                    int4_t bv;
+                    for (int v = 0; v < 2; ++v) {
+                        int4_t bv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) bv[e] = (int)wka8_dword<BITS>(d[slot], 4 * v + e);
-                    raw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][v], bv, raw, 0, 0, 0);
-                }
-                graw += raw;
-                gsx += sxg[st];
-                const int zz = wka8_zero<BITS, PGZ>(szv >> 16);
-                const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
-                // refill the slot with the unit D ahead (past the tiles: no load)
-                issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
-                if ((t + 1) % sp == 0 && t < TT) {   // the group ends with this step
-                    const int grp = t / sp;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int A = graw[i] - zz * gsx[i];
-                        const int row = 4 * g + i;
-                        if (acc_out && row < mrows && j < ntile && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A;
-                        y[i] = fmaf(sc, (float)A, y[i]);
+                        for (int e = 0; e < 4; ++e) bv[e] = (int)wka8_dword<BITS>(d[slot], 4 * v + e);
+                        raw = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[st][v], bv, raw, 0, 0, 0);
                     }
-                    graw = int4_t{0, 0, 0, 0};
-                    gsx = int4_t{0, 0, 0, 0};
+                    const int zz = wka8_zero<BITS, PGZ>(szv >> 16);
+                    const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
+                    // refill the slot with the unit D ahead (past the tiles: no load)
+                    issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
+                    // the group's int32 sums A, scaled into y when the group ends
+                    // with this step
+                    if (!SP1) {
+                        graw += raw;
+                        gsx += sxg[st];
+                    }
+                    if ((SP1 || ((t + 1) & (sp - 1)) == 0) && t < TT) {
+                        const int4_t A = SP1 ? raw - zz * sxg[st] : graw - zz * gsx;
+                        if (dump) {   // the exact group sums, for callers that ask
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int row = 4 * g + i;
+                                if (row < mrows && j < ntile && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A[i];
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[i] = fmaf(sc, (float)A[i], y[i]);
+                        if (!SP1) {
+                            graw = int4_t{0, 0, 0, 0};
+                            gsx = int4_t{0, 0, 0, 0};
+                        }
+                    }
                 }
+                // lane (g, c) of a tile holds rows 4g..4g+3, column c
+                *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
             }
-            // lane (g, c) of a tile holds rows 4g..4g+3, column c
-            *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
         }
-    }
+    };
+    if (sp == 1) tiles_loop(std::true_type{});
+    else tiles_loop(std::false_type{});
     __syncthreads();
     for (int o = threadIdx.x; o < ntile * 256; o += 512) {
         const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
