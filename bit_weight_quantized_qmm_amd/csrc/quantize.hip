@@ -10,13 +10,13 @@
 // Every rounding decision is the one the exact quotient gives
 // (round_quotient).  The codes feed qmm_pack.
 //
-// A wave covers 16 column slots of VEC adjacent columns (8-byte loads when
-// VEC = 4: 128 contiguous bytes of a row per 16 lanes) and splits a group's G
-// rows into 4 parts, one per 16-lane row of the wave; the part ranges are
-// combined with two lane shuffles.  Each lane reads its rows twice: range, then
-// codes.  The resident waves' rows exceed L2, so the second pass fetches W
-// again from beyond it (keeping the rows in registers instead measured
-// slower).
+// Two kernels.  Groups of at most 256 rows (quantize_rows_kernel): one pass
+// over W, each lane holding G / 16 rows in registers.  Larger groups
+// (quantize_kernel): a wave covers 16 column slots of VEC adjacent columns
+// (8-byte loads when VEC = 4: 128 contiguous bytes of a row per 16 lanes) and
+// splits a group's G rows into 4 parts, one per 16-lane row of the wave; the
+// part ranges are combined with two lane shuffles, and each lane reads its
+// rows twice: range, then codes.
 #include "launch.hpp"
 #include "qmm_device.hpp"
 
@@ -134,17 +134,124 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
     }
 }
 
+// One pass over W for groups of at most 256 rows: a workgroup takes 16 column
+// slots of VEC adjacent columns and splits the group's rows into 16 parts of
+// G / 16 rows, one per 16-lane row of its waves; each lane keeps its rows in
+// registers, the parts' ranges meet through lane shuffles and LDS, and the
+// codes come from the registers (W is read once: the two-pass kernel above
+// reads it twice).
+constexpr int QR_MAXR = 16;   // rows per lane: G <= 256
+template <int BITS, int VEC>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ W, uint8_t *__restrict__ codes,
+                                                            uint16_t *__restrict__ s, uint16_t *__restrict__ z, int K,
+                                                            int N, int G)
+{
+    __shared__ float rlo[4][16][VEC], rhi[4][16][VEC];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, part = tid >> 4;   // part 0..15
+    const int n0 = (blockIdx.x * 16 + c) * VEC;
+    const bool live = n0 < N;
+    const int g = blockIdx.y, ng = K / G, rp = G >> 4;
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    const size_t base = ((size_t)g * G + (size_t)part * rp) * N + n0;
+
+    uint32_t raw[QR_MAXR][VEC == 4 ? 2 : 1];
+    float lo[VEC], hi[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) lo[v] = hi[v] = 0.f;
+#pragma unroll
+    for (int r = 0; r < QR_MAXR; ++r) {
+        if (r < rp && live) {   // uniform in r; live per lane
+            const size_t at = base + (size_t)r * N;
+            if constexpr (VEC == 4) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(W + at);
+                raw[r][0] = u.x;
+                raw[r][1] = u.y;
+            } else {
+                raw[r][0] = W[at];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < (VEC == 4 ? 2 : 1); ++e) raw[r][e] = 0u;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < QR_MAXR; ++r) {
+        if (r < rp) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float w = VEC == 4 ? (float)as_half2(raw[r][v >> 1])[v & 1] : (float)as_half((uint16_t)raw[r][0]);
+                lo[v] = fminf(lo[v], w);
+                hi[v] = fmaxf(hi[v], w);
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        // the wave's four parts of a column sit 16 lanes apart; the four waves meet in LDS
+        lo[v] = fminf(lo[v], __shfl_xor(lo[v], 16));
+        lo[v] = fminf(lo[v], __shfl_xor(lo[v], 32));
+        hi[v] = fmaxf(hi[v], __shfl_xor(hi[v], 16));
+        hi[v] = fmaxf(hi[v], __shfl_xor(hi[v], 32));
+        if (lane < 16) {
+            rlo[wave][c][v] = lo[v];
+            rhi[wave][c][v] = hi[v];
+        }
+    }
+    __syncthreads();
+    float sg[VEC], inv[VEC], half[VEC], zg[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        lo[v] = fminf(fminf(rlo[0][c][v], rlo[1][c][v]), fminf(rlo[2][c][v], rlo[3][c][v]));
+        hi[v] = fmaxf(fmaxf(rhi[0][c][v], rhi[1][c][v]), fmaxf(rhi[2][c][v], rhi[3][c][v]));
+        _Float16 sh = fp16_of_double(((double)hi[v] - (double)lo[v]) / (double)QMAX);
+        if (sh == (_Float16)0.0f) sh = (_Float16)1.0f;
+        if (__builtin_isinf((float)sh)) sh = (_Float16)65504.0f;
+        sg[v] = (float)sh;
+        inv[v] = 1.0f / sg[v];
+        half[v] = 0.5f * sg[v];
+        zg[v] = fminf(fmaxf(round_quotient(-lo[v], sg[v], inv[v], half[v]), 0.f), QMAX);
+        if (part == 0 && n0 + v < N) {
+            s[(size_t)(n0 + v) * ng + g] = as_u16(sh);
+            z[(size_t)(n0 + v) * ng + g] = as_u16((_Float16)zg[v]);
+        }
+    }
+    if (!live) return;
+#pragma unroll
+    for (int r = 0; r < QR_MAXR; ++r) {
+        if (r < rp) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float w = VEC == 4 ? (float)as_half2(raw[r][v >> 1])[v & 1] : (float)as_half((uint16_t)raw[r][0]);
+                const float q = fminf(fmaxf(round_quotient(w, sg[v], inv[v], half[v]) + zg[v], 0.f), QMAX);
+                packed |= (uint32_t)q << (8 * v);
+            }
+            const size_t at = base + (size_t)r * N;
+            if constexpr (VEC == 4)
+                *reinterpret_cast<uint32_t *>(codes + at) = packed;
+            else
+                codes[at] = (uint8_t)packed;
+        }
+    }
+}
+
 hipError_t launch_quantize(const uint16_t *W, uint8_t *codes, uint16_t *s, uint16_t *z, int K, int N, int bits, int G,
                            hipStream_t st)
 {
     // four columns per thread when every row of W and of the codes stays 8- and
     // 4-byte aligned
     const bool vec = N % 4 == 0 && reinterpret_cast<uintptr_t>(W) % 8 == 0 && reinterpret_cast<uintptr_t>(codes) % 4 == 0;
-    const int per_block = vec ? 256 : 64;   // 4 waves of 16 column slots
+    const bool one_pass = G <= 16 * QR_MAXR;   // G % 32 == 0: 2 .. 16 rows per lane
+    const int per_block = one_pass ? (vec ? 64 : 16) : (vec ? 256 : 64);   // 16 or 4 x 16 column slots
     const dim3 block(256), grid((unsigned)((N + per_block - 1) / per_block), (unsigned)(K / G));
 #define QMM_Q(B)                                                                                                \
     do {                                                                                                        \
-        if (vec)                                                                                                \
+        if (one_pass && vec)                                                                                    \
+            hipLaunchKernelGGL((quantize_rows_kernel<B, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);      \
+        else if (one_pass)                                                                                      \
+            hipLaunchKernelGGL((quantize_rows_kernel<B, 1>), grid, block, 0, st, W, codes, s, z, K, N, G);      \
+        else if (vec)                                                                                           \
             hipLaunchKernelGGL((quantize_kernel<B, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);           \
         else                                                                                                    \
             hipLaunchKernelGGL((quantize_kernel<B, 1>), grid, block, 0, st, W, codes, s, z, K, N, G);           \
