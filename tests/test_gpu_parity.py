@@ -593,10 +593,13 @@ def check_quantize(q, orc, W, bits, G):
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
-@pytest.mark.parametrize("K,N,G", [(256, 300, 64), (1024, 70, 128), (96, 513, 32)])
+@pytest.mark.parametrize("K,N,G", [(256, 300, 64), (1024, 70, 128), (96, 513, 32), (480, 132, 96), (1600, 77, 160),
+                                   (512, 260, 256), (1024, 68, 512), (2048, 33, 1024)])
 def test_quantize_small(q, orc, bits, K, N, G):
     """Codes, s and z bit-exact on LLM-like weights: several column blocks and
-    a ragged column tail."""
+    a ragged column tail; groups of 2 to 16 rows per lane in the one-pass
+    kernel (G 32 .. 256, odd counts at G 96 and 160) and the two-pass kernel
+    beyond (G 512, 1024)."""
     rng = np.random.default_rng(synthetic.seed_for(99, bits, K + N))
     W = rng.normal(0.0, 0.02, (K, N)).astype(np.float16)
     W[:, ::7] *= np.float16(8.0)                   # a few wide columns
