@@ -300,10 +300,14 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
                 }
             }
             int4_t *dst = reinterpret_cast<int4_t *>(smem + (it0 < R ? (uint32_t)it * 64u : xs_bytes + 64u));
+            // 16-byte chunk q of item it sits at q ^ (bits 2..3 of it): 16
+            // neighbouring lanes then write (and read back) 16 distinct chunk
+            // slots instead of 4 (a 4-way LDS bank conflict)
+            const int sw = (it0 >> 2) & 3;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                dst[q] = int4_t{(int)as_u32(xs[4 * q]), (int)as_u32(xs[4 * q + 1]), (int)as_u32(xs[4 * q + 2]),
-                                (int)as_u32(xs[4 * q + 3])};
+                dst[q ^ sw] = int4_t{(int)as_u32(xs[4 * q]), (int)as_u32(xs[4 * q + 1]), (int)as_u32(xs[4 * q + 2]),
+                                     (int)as_u32(xs[4 * q + 3])};
             c1[it] = a1;
             if (PGZ) c2[it] = a2;
         }
@@ -317,9 +321,10 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
     for (int j = 0; j < RPL; ++j) {
         const int r = lane + 64 * j;
         const int4_t *src = reinterpret_cast<const int4_t *>(smem + (r < R ? (uint32_t)r * 64u : xs_bytes));
+        const int sw = (r >> 2) & 3;   // the staging's chunk order (the zero slot reads zeros anyway)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int4_t v = src[q];
+            const int4_t v = src[q ^ sw];
 #pragma unroll
             for (int e = 0; e < 4; ++e) xv[j][4 * q + e] = as_half2((uint32_t)v[e]);
         }
