@@ -336,9 +336,9 @@ static int gemm_cus()
 // at the end): 128 x 256 (8 waves of 32 columns), 128 x 128 in 2 K parts,
 // 64 x 128 (8 waves of 16 columns), 64 x 64 in 2 parts, 64 x 32 in 4, and
 // 32 x 16 in 8 parts.  The first whose grid reaches 4/5 of the CUs is taken,
-// else the last.  Measured at K = 4096, k 4 (us): M 128: 23.7 -> 18.8;
-// M 256: 25.3 -> 23.6; M 1024: 59.2 -> 56.5; M 100, N 1000: 22.6 -> 12.5;
-// M 512 and M 2048 keep their tiles.
+// else the last.  Measured at K = N = 4096, k 4 (us, without -> with the K
+// parts): M 128: 23.7 -> 20.1; M 256: 25.3 -> 25.1; M 1024: 59.2 -> 56.5;
+// M 100, N 1000: 22.6 -> 12.6; M 512 and M 2048 keep their tiles.
 template <int BITS, int FMT>
 static hipError_t gemm_dispatch(const GemvArgs &a, hipStream_t st)
 {
