@@ -89,10 +89,11 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // Index of the group that holds 32-code run r when a group spans gr runs
 // (gr = G / 32), i.e. r / gr, without an integer division (which costs about
-// 20 VALU instructions): inv = 1 / gr rounded to fp32, then
-// trunc((r + 1/2) inv).  (r + 1/2) / gr lies at least 1/(2 gr) from any
-// integer, and the two fp32 roundings move it by at most (r + 1/2) 2^-23 / gr,
-// less than that for r < 2^22 (run indices here stay below 2^16 + 8).
+// 20 VALU instructions): inv = 1 / gr in fp32, then trunc((r + 1/2) inv).
+// (r + 1/2) / gr lies at least 1/(2 gr) from any integer, and the fp32
+// roundings (a few units in the last place of inv, one of the product) move it
+// by at most about (r + 1/2) 2^-21 / gr, less than that for r < 2^20 (run
+// indices here stay below 2^16 + 8; checked exhaustively on the host).
 __device__ __forceinline__ float run_group_inv(int G) { return 1.0f / (float)(G >> 5); }
 __device__ __forceinline__ int run_group(int r, float inv) { return (int)(((float)r + 0.5f) * inv); }
 
