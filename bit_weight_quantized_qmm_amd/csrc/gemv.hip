@@ -208,11 +208,16 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
     const int w = wg * 4 + wave;
     const int ncw = w < N ? (N - 1 - w) / W + 1 : 0;    // columns of this wave (<= 64)
 
-    // LDS: xs [R] runs x 64 B | 64 B zeros | 64 B dummy | c1 [R] + 4 | c2 [R] + 4 (PGZ) | rmax [4]
-    const uint32_t xs_bytes = (uint32_t)R * 64u;
+    // LDS: xs [RX] runs x 64 B | 64 B zeros | 64 B dummy | c1 [RX] + 4 | c2 [RX] + 4 (PGZ) | rmax [4].
+    // XL (more than 8 runs per lane): X stays in LDS and every lane reads its
+    // runs from there for each column; the runs are staged up to 64 RPL (zeros
+    // past K), so that each run's address is a base plus a constant.
+    constexpr bool XL = RPL > 8;
+    const int RX = XL ? 64 * RPL : R;
+    const uint32_t xs_bytes = (uint32_t)RX * 64u;
     float *c1 = reinterpret_cast<float *>(smem + xs_bytes + 128);
-    float *c2 = c1 + R + 4;
-    uint32_t *rmax = reinterpret_cast<uint32_t *>(c2 + (PGZ ? R + 4 : 0));
+    float *c2 = c1 + RX + 4;
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(c2 + (PGZ ? RX + 4 : 0));
 
     // 1. activations for the staging (IPT runs per thread)
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)K * 2u);
@@ -254,8 +259,12 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
         }
         __builtin_amdgcn_sched_barrier(0);   // keep slots in issue order (loads complete in order)
     };
+    // (with 16 runs per lane the first columns go out after the staging: their
+    // 16 k dwords and X's 64 would not fit in the registers together)
+    if constexpr (RPL <= 8) {
 #pragma unroll
-    for (int q = 0; q < D; ++q) issue(q, q);
+        for (int q = 0; q < D; ++q) issue(q, q);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. staging: waves that own items convert X to slot order with bias sums,
@@ -276,9 +285,9 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        if (256 * i + 64 * wave < R) {               // wave-uniform
+        if (256 * i + 64 * wave < RX) {              // wave-uniform
             const int it0 = tid + 256 * i;
-            const int it = it0 < R ? it0 : R;        // R = the dummy item
+            const int it = it0 < RX ? it0 : RX;      // RX = the dummy item
             half2_t xs[16];
             float a1 = 0.f, a2 = 0.f;
             if constexpr (FMT != 0) {   // float codes: X in code order, no bias
@@ -299,7 +308,7 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
                     a1 = __builtin_amdgcn_fdot2(xs[p], slot_bias<BITS>(p, zdef), a1, false);
                 }
             }
-            int4_t *dst = reinterpret_cast<int4_t *>(smem + (it0 < R ? (uint32_t)it * 64u : xs_bytes + 64u));
+            int4_t *dst = reinterpret_cast<int4_t *>(smem + (it0 < RX ? (uint32_t)it * 64u : xs_bytes + 64u));
             // 16-byte chunk q of item it sits at q ^ (bits 2..3 of it): 16
             // neighbouring lanes then write (and read back) 16 distinct chunk
             // slots instead of 4 (a 4-way LDS bank conflict)
@@ -314,11 +323,18 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
     }
     __syncthreads();
 
-    // 4. this lane's activations and bias sums (runs past K read the zero slot)
-    half2_t xv[RPL][16];
-    float b1[RPL], b2[RPL];
+    if constexpr (RPL > 8) {
 #pragma unroll
-    for (int j = 0; j < RPL; ++j) {
+        for (int q = 0; q < D; ++q) issue(q, q);
+    }
+
+    // 4. this lane's activations and bias sums (runs past K read the zero slot):
+    //    in VGPRs up to 8 runs per lane; beyond (XL, K up to 32768) they stay
+    //    in LDS and are read for every column
+    constexpr int RV = XL ? 1 : RPL;
+    half2_t xv[RV][16];
+    float b1[RV], b2[RV];
+    auto run_x = [&](int j, half2_t (&xj)[16], float &bj1, float &bj2) {
         const int r = lane + 64 * j;
         const int4_t *src = reinterpret_cast<const int4_t *>(smem + (r < R ? (uint32_t)r * 64u : xs_bytes));
         const int sw = (r >> 2) & 3;   // the staging's chunk order (the zero slot reads zeros anyway)
@@ -326,12 +342,32 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
         for (int q = 0; q < 4; ++q) {
             const int4_t v = src[q ^ sw];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xv[j][4 * q + e] = as_half2((uint32_t)v[e]);
+            for (int e = 0; e < 4; ++e) xj[4 * q + e] = as_half2((uint32_t)v[e]);
         }
         const int rc = r < R ? r : R;               // c1[R] is written only by the dummy item: mask it
-        b1[j] = r < R ? c1[rc] : 0.f;
-        b2[j] = (PGZ && r < R) ? c2[rc] : 0.f;
+        bj1 = r < R ? c1[rc] : 0.f;
+        bj2 = (PGZ && r < R) ? c2[rc] : 0.f;
+    };
+    if constexpr (!XL) {
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) run_x(j, xv[j], b1[j], b2[j]);
     }
+    // XL: chunk q of this lane's run j at xq[q] + 4096 j (the swizzle depends
+    // on bits 2..3 of the run index, the same for every j), its bias sums at
+    // c1 / c2 [lane + 64 j]
+    const uint8_t *xq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xq[q] = smem + (uint32_t)lane * 64u + 16u * (uint32_t)(q ^ ((lane >> 2) & 3));
+    auto run_xl = [&](int j, half2_t (&xj)[16], float &bj1, float &bj2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4_t v = *reinterpret_cast<const int4_t *>(xq[q] + 4096 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xj[4 * q + e] = as_half2((uint32_t)v[e]);
+        }
+        bj1 = c1[lane + 64 * j];
+        bj2 = PGZ ? c2[lane + 64 * j] : 0.f;
+    };
 
     // 5. stream the wave's columns: compute column i while columns i+1..i+D-1 load
     float yout = 0.f;
@@ -341,26 +377,38 @@ __device__ __forceinline__ void m1_body(const uint16_t *__restrict__ X, const ui
             const int i = i0 + q;                     // columns past ncw compute on zeros
             {
                 float y = 0.f;
+                // XL: run j's activations come from LDS, read one run ahead into
+                // two alternating register sets; the scheduling barrier at the end
+                // of each run keeps the compiler from hoisting all 16 runs' reads
+                half2_t xl[2][16];
+                float bl1[2] = {0.f, 0.f}, bl2[2] = {0.f, 0.f};
+                if constexpr (XL) run_xl(0, xl[0], bl1[0], bl2[0]);
 #pragma unroll
                 for (int j = 0; j < RPL; ++j) {
+                    if constexpr (XL) {
+                        if (j + 1 < RPL) run_xl(j + 1, xl[(j + 1) & 1], bl1[(j + 1) & 1], bl2[(j + 1) & 1]);
+                    }
                     uint32_t h[16];
                     if constexpr (FMT != 0) {
                         fp_run_to_half2<FMT>(d[q][j], h);
                     } else {
                         run_to_half2<BITS>(d[q][j], h);
                     }
+                    const half2_t (&xj)[16] = XL ? xl[j & 1] : xv[XL ? 0 : j];
+                    const float bj1 = XL ? bl1[j & 1] : b1[XL ? 0 : j], bj2 = XL ? bl2[j & 1] : b2[XL ? 0 : j];
                     float a = 0.f, a_odd = 0.f;
 #pragma unroll
                     for (int p = 0; p < 16; p += 2) {
-                        a = __builtin_amdgcn_fdot2(xv[j][p], as_half2(h[p]), a, false);
-                        a_odd = __builtin_amdgcn_fdot2(xv[j][p + 1], as_half2(h[p + 1]), a_odd, false);
+                        a = __builtin_amdgcn_fdot2(xj[p], as_half2(h[p]), a, false);
+                        a_odd = __builtin_amdgcn_fdot2(xj[p + 1], as_half2(h[p + 1]), a_odd, false);
                     }
                     if constexpr (FMT != 0) {   // exact code values: no bias
                         y = fmaf((float)as_half(sv[q][j]), a + a_odd, y);
                     } else {
-                        const float bias = PGZ ? fmaf((float)as_half(zv[q][j]), b2[j], b1[j]) : b1[j];
+                        const float bias = PGZ ? fmaf((float)as_half(zv[q][j]), bj2, bj1) : bj1;
                         y = fmaf((float)as_half(sv[q][j]), (a + a_odd) - bias, y);
                     }
+                    if constexpr (XL) __builtin_amdgcn_sched_barrier(0);
                 }
                 issue(q, i + D);                      // refill this slot (zeros past the wave's columns)
                 y = wave_sum_dpp(y);
@@ -384,7 +432,7 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
 // 8 / 4 / 2 / 1 for RPL 1 / 2 / 4 / 8; 4 for RPL 4 at k <= 2, whose columns
 // carry few bytes) and items of X staging per thread.
 __host__ __device__ constexpr int m1_depth(int bits, int rpl) { return rpl <= 1 ? 8 : rpl == 2 ? 4 : rpl == 4 ? (bits <= 2 ? 4 : 2) : 1; }
-__host__ __device__ constexpr int m1_ipt(int rpl) { return rpl == 8 ? 2 : 1; }
+__host__ __device__ constexpr int m1_ipt(int rpl) { return rpl == 16 ? 4 : rpl == 8 ? 2 : 1; }
 
 // Several M = 1 products in one launch (qmm_gemv_grouped): workgroups
 // wg0[p] .. wg0[p + 1] - 1 serve problem p, each running the decode body above
@@ -1085,15 +1133,16 @@ static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const size_t lds = m1_lds_bytes(a.K, PGZ);
+    const size_t lds = m1_lds_bytes(RPL > 8 ? 32 * 64 * RPL : a.K, PGZ);   // RPL 16: runs staged up to 64 RPL
     const dim3 block(256), grid(m1_grid(a.N));
     hipLaunchKernelGGL((gemv_m1_kernel<BITS, RPL, D, IPT, PGZ, FMT>), grid, block, lds, st, a.X, a.wq, a.s, a.z, a.Y, a.K,
                        a.N, a.G);
     return hipGetLastError();
 }
 
-// M = 1 with K <= 16384 and at most 64 columns per wave: RPL = runs per lane
-// (1, 2, 4, 8), D = 8 / RPL columns in flight per wave; 4 for RPL = 4 and
+// M = 1 with K <= 32768 and at most 64 columns per wave: RPL = runs per lane
+// (1, 2, 4, 8; 16 with X read from LDS per column), D = 8 / RPL columns in
+// flight per wave (1 at RPL 16); 4 for RPL = 4 and
 // k <= 2, whose columns carry few bytes (k = 2 on the 70B MLP-up shape: 19.4
 // -> 17.2 us; 8 in flight, or two workgroups per CU, measured slower).
 template <int BITS, bool PGZ>
@@ -1104,7 +1153,8 @@ static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
     if (rpl_need <= 1) return gemv_m1_go<BITS, 1, m1_depth(BITS, 1), m1_ipt(1), PGZ>(a, st);
     if (rpl_need <= 2) return gemv_m1_go<BITS, 2, m1_depth(BITS, 2), m1_ipt(2), PGZ>(a, st);
     if (rpl_need <= 4) return gemv_m1_go<BITS, 4, m1_depth(BITS, 4), m1_ipt(4), PGZ>(a, st);
-    return gemv_m1_go<BITS, 8, m1_depth(BITS, 8), m1_ipt(8), PGZ>(a, st);
+    if (rpl_need <= 8) return gemv_m1_go<BITS, 8, m1_depth(BITS, 8), m1_ipt(8), PGZ>(a, st);
+    return gemv_m1_go<BITS, 16, m1_depth(BITS, 16), m1_ipt(16), PGZ>(a, st);
 }
 
 // Grouped M = 1 products: the CUs are shared out in proportion to each
@@ -1237,7 +1287,7 @@ template <int BITS>
 static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
 {
     const int R = a.K / 32, TT = (R + 3) / 4;
-    if (a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
+    if (a.M == 1 && R <= 1024 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
         (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64)
         return a.z ? gemv_m1_launch<BITS, true>(a, st) : gemv_m1_launch<BITS, false>(a, st);
     if (a.M >= 2 && a.G % 128 == 0 && a.K <= 64 * 128 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)

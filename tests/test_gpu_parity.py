@@ -116,8 +116,22 @@ def test_gemv_small(q, orc, bits, M, pgz, K, N, G):
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("K,N,G,pgz", [(16416, 300, 32, False), (20480, 77, 128, True), (28672, 130, 128, False)],
+                         ids=lambda v: str(v))
+def test_gemv_m1_runs_in_lds(q, orc, bits, K, N, G, pgz):
+    """M = 1 beyond 8 runs per lane (K > 16384): the decode kernel with 16 runs
+    per lane, X read from LDS for every column; a ragged run count (K 16416,
+    513 runs), the 70B MLP-down K, and both zero-point forms."""
+    c = synthetic.make_case(1, K, N, bits, G, synthetic.seed_for(101, bits, K // 32), per_group_z=pgz)
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, G)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
 def test_gemv_m1_long_k(q, orc, bits):
-    """K beyond the single-wave M = 1 kernel's register slice: the MFMA path with several K passes."""
+    """K = 32768 (1024 runs, 16 per lane): the decode kernel's largest K, with
+    X read from LDS for every column."""
     c = synthetic.make_case(1, 32768, 24, bits, 128, synthetic.seed_for(92, bits), per_group_z=True)
     Y = run_product(q, q.gemv, c)
     ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, 128)
