@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t *__restrict
 // 8 / 4 / 2 / 1 for RPL 1 / 2 / 4 / 8; 4 for RPL 4 at k <= 2, whose columns
 // carry few bytes) and items of X staging per thread.
 __host__ __device__ constexpr int m1_depth(int bits, int rpl) { return rpl <= 1 ? 8 : rpl == 2 ? 4 : rpl == 4 ? (bits <= 2 ? 4 : 2) : 1; }
-__host__ __device__ constexpr int m1_ipt(int rpl) { return rpl == 16 ? 4 : rpl == 8 ? 2 : 1; }
+__host__ __device__ constexpr int m1_ipt(int rpl) { return rpl == 16 ? 4 : rpl == 12 ? 3 : rpl == 8 ? 2 : 1; }
 
 // Several M = 1 products in one launch (qmm_gemv_grouped): workgroups
 // wg0[p] .. wg0[p + 1] - 1 serve problem p, each running the decode body above
@@ -1141,8 +1141,8 @@ static hipError_t gemv_m1_go(const GemvArgs &a, hipStream_t st)
 }
 
 // M = 1 with K <= 32768 and at most 64 columns per wave: RPL = runs per lane
-// (1, 2, 4, 8; 16 with X read from LDS per column), D = 8 / RPL columns in
-// flight per wave (1 at RPL 16); 4 for RPL = 4 and
+// (1, 2, 4, 8; 12 and 16 with X read from LDS per column), D = 8 / RPL
+// columns in flight per wave (1 beyond 8); 4 for RPL = 4 and
 // k <= 2, whose columns carry few bytes (k = 2 on the 70B MLP-up shape: 19.4
 // -> 17.2 us; 8 in flight, or two workgroups per CU, measured slower).
 template <int BITS, bool PGZ>
@@ -1154,6 +1154,7 @@ static hipError_t gemv_m1_launch(const GemvArgs &a, hipStream_t st)
     if (rpl_need <= 2) return gemv_m1_go<BITS, 2, m1_depth(BITS, 2), m1_ipt(2), PGZ>(a, st);
     if (rpl_need <= 4) return gemv_m1_go<BITS, 4, m1_depth(BITS, 4), m1_ipt(4), PGZ>(a, st);
     if (rpl_need <= 8) return gemv_m1_go<BITS, 8, m1_depth(BITS, 8), m1_ipt(8), PGZ>(a, st);
+    if (rpl_need <= 12) return gemv_m1_go<BITS, 12, m1_depth(BITS, 12), m1_ipt(12), PGZ>(a, st);
     return gemv_m1_go<BITS, 16, m1_depth(BITS, 16), m1_ipt(16), PGZ>(a, st);
 }
 
