@@ -112,9 +112,10 @@ qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, 
 /* Decode-shaped product, 1 <= M <= 16 (else QMM_ERR_INVALID_ARG):
  * Y = X . dequant(Wq), fp32 accumulation.  Eq. (5) of BitLLM Sec. 2.2 with
  * per-group s, z, factored so that the zero-point bias leaves a sum:
- *   M == 1: a split-K VALU kernel (v_dot2 of the activations, scaled by 2^-p,
- *           with the fp16 code patterns 1024 + q 2^p; the bias of each 32-code
- *           run is subtracted from its partial sum, which is then scaled).
+ *   M == 1, K <= 32768, N <= 64 x 4 x (CU count): a split-K VALU kernel
+ *           (v_dot2 of the activations, scaled by 2^-p, with the fp16 code
+ *           patterns 1024 + q 2^p; the bias of each 32-code run is subtracted
+ *           from its partial sum, which is then scaled).
  *   2 <= M <= 16 with G % 128 == 0 and K <= 8192: f16 MFMA with M padded to
  *           16, the raw code patterns as B operand and one correction MFMA per
  *           128 rows of K.
