@@ -799,7 +799,7 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 // Launch selection.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// M <= 16 on MFMA, G % 128 == 0, K <= 8192.  One v_mfma_f32_16x16x32_f16 tile
+// M <= 16 on MFMA, G % 128 == 0, any K (passes of 8192 rows).  One v_mfma_f32_16x16x32_f16 tile
 // is 16 rows (X, zero past M) by 16 columns.  The B operand is the raw fp16
 // code pattern 1024 + q 2^p of each lane's run (no per-weight arithmetic past
 // the unpack); the A operand is X in slot order scaled by 2^-p.  Per 128-row
@@ -813,9 +813,9 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 // Floating-point codes (FMT != 0): A is X in code order and B the codes'
 // exact values from the packed fp4 / fp8 conversions; there is no correction.
 //
-// A workgroup of 8 waves owns tpw <= T consecutive 16-column tiles; wave w
-// owns K steps w*S .. w*S + S - 1 of every tile and keeps the A fragments of
-// that K slice in registers.  The s and z of the workgroup's columns are
+// A workgroup of 8 waves owns tpw <= T consecutive 16-column tiles; in each
+// pass of 8 S K steps, wave w owns steps w*S .. w*S + S - 1 of the pass for
+// every tile and keeps the A fragments of that K slice in registers.  The s and z of the workgroup's columns are
 // staged once in LDS (read along the group index, so every load is a whole
 // column's run of groups), which leaves only the weight runs in the per-unit
 // stream: units (tile, step) pass through a ring of D weight loads in flight,
@@ -825,9 +825,9 @@ __global__ __launch_bounds__(512) void gemv_rows_kernel(const uint16_t *__restri
 static int num_cus();
 
 constexpr int MMA_WAVES = 8;   // waves per workgroup of the M <= 16 MFMA GEMV
-constexpr int MMA_MAXNG = 64;  // groups per column: K <= 8192, G >= 128
+constexpr int MMA_MAXNG = 64;  // groups per column and pass: 8192 rows, G >= 128
 
-template <int BITS, int S, int T, int D, bool PGZ, int FMT = 0>
+template <int BITS, int S, int T, int D, bool PGZ, int FMT = 0, bool MP = false>
 __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ wq,
                                                        const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
                                                        uint16_t *__restrict__ Y, int M, int K, int N, int G, int tpw)
@@ -854,14 +854,27 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     const __amdgpu_buffer_rsrc_t zr = make_rsrc(PGZ ? z : s, PGZ ? (uint32_t)(N * ng * 2) : 0u);
     const uint32_t zdef_bits = (uint32_t)as_u16((_Float16)(float)(1u << (BITS - 1)));
 
+    // K in passes of MMA_WAVES * S steps (one pass up to K = 8192 at S = 8):
+    // every pass stages its groups' s | z, its X fragments and row exponents,
+    // and streams the workgroup's tiles over its K range; each wave adds the
+    // pass's tile sums, scaled back to X's units, into its own LDS slots.
+    // (MP: more than one pass; the one-pass form keeps the row scaling for the
+    // epilogue and spends no registers on it inside the loop)
+    const int KS = MMA_WAVES * S, P = MP ? (((R + 3) >> 2) + KS - 1) / KS : 1;
+    for (int pass = 0; pass < P; ++pass) {
+    const int tb = pass * KS;                       // first step of the pass
+    const int g0 = min(run_group(4 * tb, ginv), ng - 1);   // first group of the pass
+    if (pass > 0) __syncthreads();                  // the previous pass's table and row maxima are read
+
     // s and z of the workgroup's columns: wave w reads columns w, w + 8, ...,
-    // lane l holding group l (past ng, or past the workgroup's columns: zeros)
+    // lane l holding group g0 + l (past ng, or past the workgroup's columns: zeros)
     constexpr int SZE = T * 16 / MMA_WAVES;
     uint32_t sraw[SZE], zraw[SZE];
 #pragma unroll
     for (int e = 0; e < SZE; ++e) {
         const int cl = wave + MMA_WAVES * e;
-        const uint32_t off = (lane < ng && cl < 16 * ntile) ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)lane) * 2u : OOB;
+        const uint32_t off = (g0 + lane < ng && cl < 16 * ntile)
+                                 ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)(g0 + lane)) * 2u : OOB;
         sraw[e] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
         zraw[e] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : zdef_bits;
     }
@@ -873,7 +886,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     // and meets zero activations; units past the workgroup's tiles load nothing.
     uint32_t d[D][BITS];
     auto issue = [&](int j, int st, int slot) {
-        const int t = wave * S + st;
+        const int t = tb + wave * S + st;
         const uint32_t col = (uint32_t)(16 * (tile0 + j) + c);
         // default cache policy: a unit's runs cut cache lines that the wave's next
         // unit reads, and with the non-temporal hint those lines were fetched
@@ -886,7 +899,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
     for (int e = 0; e < SZE; ++e) {
         const int cl = wave + MMA_WAVES * e;
-        if (lane < ng) sz[lane * SZW + cl] = (sraw[e] & 0xffffu) | (zraw[e] << 16);
+        if (g0 + lane < ng) sz[lane * SZW + cl] = (sraw[e] & 0xffffu) | (zraw[e] << 16);
     }
 
     // X run of this lane for step t: row c, run 4 t + g (zeros past M or K)
@@ -904,7 +917,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     {
         uint32_t xa[S][16];
 #pragma unroll
-        for (int st = 0; st < S; ++st) load_xrun(wave * S + st, xa[st]);
+        for (int st = 0; st < S; ++st) load_xrun(tb + wave * S + st, xa[st]);
         int erow = 0;
         if constexpr (FMT == 0) {
             uint32_t mx = 0;
@@ -964,6 +977,19 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
         }
     }
 
+    // 2^-e of this lane's output rows 4g..4g+3 in this pass (the rows' X was
+    // scaled by 2^e)
+    float oscale[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (FMT == 0 && MP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int w = 0; w < MMA_WAVES; ++w) mx = max(mx, rmx[w][4 * g + i]);
+            oscale[i] = __builtin_ldexpf(1.0f, -row_exponent(mx));
+        }
+    }
+
     // UT tiles per loop iteration keep every ring slot a compile-time index
     constexpr int UT = D > S ? D / S : 1;
 #pragma unroll 1
@@ -975,8 +1001,8 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
             for (int st = 0; st < S; ++st) {
                 const int slot = (jj * S + st) % D;
-                const int t = wave * S + st;
-                const uint32_t szv = sz[min(run_group(4 * t, ginv), ng - 1) * SZW + 16 * j + c];
+                const int t = tb + wave * S + st;
+                const uint32_t szv = sz[(min(run_group(4 * t, ginv), ng - 1) - g0) * SZW + 16 * j + c];
                 uint32_t h[16];
                 if constexpr (FMT != 0) {
                     fp_run_to_half2<FMT>(d[slot], h);
@@ -1035,9 +1061,17 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
                 for (int i = 0; i < 4; ++i) y[i] = fmaf(sc, acc[i], y[i]);
             }
             // lane (g, c) of a tile holds rows 4g..4g+3, column c
-            *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
+            float4_t *rs = reinterpret_cast<float4_t *>(&red[wave][j][lane][0]);
+            if constexpr (MP) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] *= oscale[i];   // exact: powers of two
+                *rs = pass == 0 ? y : *rs + y;
+            } else {
+                *rs = y;
+            }
         }
     }
+    }   // passes
     // add the 8 waves' partial tiles
     __syncthreads();
     for (int o = threadIdx.x; o < ntile * 256; o += 64 * MMA_WAVES) {
@@ -1047,7 +1081,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 #pragma unroll
         for (int w = 0; w < MMA_WAVES; ++w) v += red[w][j][l][i];
         const int n = 16 * (tile0 + j) + col;
-        if constexpr (FMT == 0) {   // undo the row's 2^e
+        if constexpr (FMT == 0 && !MP) {   // undo the row's 2^e (one pass)
             uint32_t mx = 0;
 #pragma unroll
             for (int w = 0; w < MMA_WAVES; ++w) mx = max(mx, rmx[w][m]);
@@ -1063,12 +1097,12 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
 // N 28672) at M = 8 and 16 (wider codes leave fewer free registers).
 __host__ __device__ constexpr int mma_ring(int bits) { return bits <= 3 || bits == 7 ? 8 : bits == 8 ? 2 : 4; }
 
-template <int BITS, int S, int T, bool PGZ, int FMT>
+template <int BITS, int S, int T, bool PGZ, int FMT, bool MP = false>
 static hipError_t gemv_mma_go(const GemvArgs &a, int grid, int tpw, hipStream_t st)
 {
     constexpr int D0 = mma_ring(BITS);
     constexpr int D = D0 < S * T ? D0 : S * T;
-    hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ, FMT>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
+    hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ, FMT, MP>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
                        a.M, a.K, a.N, a.G, tpw);
     return hipGetLastError();
 }
@@ -1082,9 +1116,10 @@ static hipError_t gemv_mma_pick_t(const GemvArgs &a, int grid, int tpw, hipStrea
     return gemv_mma_go<BITS, S, 8, PGZ, FMT>(a, grid, tpw, st);
 }
 
-// Requires G % 128 == 0 and K <= 8192 (8 waves x 8 steps of 128 rows).  One
-// batch of at most 8 tiles per workgroup; past 8 x (CU count) tiles the
-// workgroups run in several rounds.
+// Requires G % 128 == 0.  One pass up to K = 8192 (8 waves x 8 steps of 128
+// rows); beyond, passes of 4096 rows (4 steps per wave: the pass form's
+// registers at 8 steps per wave spill).  One batch of at most 8 tiles per
+// workgroup; past 8 x (CU count) tiles the workgroups run in several rounds.
 template <int BITS, bool PGZ, int FMT = 0>
 static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
 {
@@ -1093,6 +1128,10 @@ static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
     const int tiles = (a.N + 15) / 16;
     const int tpw = std::min(8, std::max(1, (tiles + num_cus() - 1) / num_cus()));
     const int grid = (tiles + tpw - 1) / tpw;
+    if (steps > 8) {
+        if (tpw <= 2) return gemv_mma_go<BITS, 4, 2, PGZ, FMT, true>(a, grid, tpw, st);
+        return gemv_mma_go<BITS, 4, 8, PGZ, FMT, true>(a, grid, tpw, st);
+    }
     if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ, FMT>(a, grid, tpw, st);
     if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ, FMT>(a, grid, tpw, st);
     if (steps <= 4) return gemv_mma_pick_t<BITS, 4, PGZ, FMT>(a, grid, tpw, st);
@@ -1291,7 +1330,7 @@ static hipError_t gemv_dispatch(const GemvArgs &a, hipStream_t st)
     if (a.M == 1 && R <= 1024 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
         (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64)
         return a.z ? gemv_m1_launch<BITS, true>(a, st) : gemv_m1_launch<BITS, false>(a, st);
-    if (a.M >= 2 && a.G % 128 == 0 && a.K <= 64 * 128 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
+    if (a.M >= 2 && a.G % 128 == 0 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
         return a.z ? gemv_mma_launch<BITS, true>(a, st) : gemv_mma_launch<BITS, false>(a, st);
     if (a.M <= 4) {
         int T = 1;
@@ -1318,7 +1357,7 @@ template <int BITS, int FMT>
 static hipError_t gemv_small_fp(const GemvArgs &a, hipStream_t st)
 {
     const int R = a.K / 32;
-    if (a.M >= 2 && a.M <= 16 && a.G % 128 == 0 && a.K <= 64 * 128 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
+    if (a.M >= 2 && a.M <= 16 && a.G % 128 == 0 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu)
         return gemv_mma_launch<BITS, false, FMT>(a, st);
     if (!(a.M == 1 && R <= 512 && (size_t)a.N * R * 4 * BITS < 0x7fffffffu &&
           (a.N + 4 * m1_grid(a.N) - 1) / (4 * m1_grid(a.N)) <= 64))

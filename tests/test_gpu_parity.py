@@ -129,6 +129,19 @@ def test_gemv_m1_runs_in_lds(q, orc, bits, K, N, G, pgz):
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("M,K,N,pgz", [(2, 12288, 70, True), (8, 28672, 300, False), (16, 9216, 33, True)],
+                         ids=lambda v: str(v))
+def test_gemv_batched_long_k(q, orc, bits, M, K, N, pgz):
+    """2 <= M <= 16 past K = 8192: the MFMA GEMV in passes of 4096 rows, each
+    with its own s | z table and row exponents (K 9216: a last pass of one
+    step per wave; K 28672: the 70B MLP-down)."""
+    c = synthetic.make_case(M, K, N, bits, 128, synthetic.seed_for(102, bits, M * 100 + K // 1024), per_group_z=pgz)
+    Y = run_product(q, q.gemv, c)
+    ref = orc.qmm(c["X"], orc.pack(c["codes"], bits), c["s"], c["z"], bits, 128)
+    assert rel_err(Y, ref) <= TOL
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
 def test_gemv_m1_long_k(q, orc, bits):
     """K = 32768 (1024 runs, 16 per lane): the decode kernel's largest K, with
     X read from LDS for every column."""
