@@ -116,9 +116,9 @@ qmm_status qmm_unpack(const uint32_t *wq, uint8_t *codes, int64_t K, int64_t N, 
  *           (v_dot2 of the activations, scaled by 2^-p, with the fp16 code
  *           patterns 1024 + q 2^p; the bias of each 32-code run is subtracted
  *           from its partial sum, which is then scaled).
- *   2 <= M <= 16 with G % 128 == 0 and K <= 8192: f16 MFMA with M padded to
- *           16, the raw code patterns as B operand and one correction MFMA per
- *           128 rows of K.
+ *   2 <= M <= 16 with G % 128 == 0: f16 MFMA with M padded to 16, the raw
+ *           code patterns as B operand and one correction MFMA per 128 rows of
+ *           K (K beyond 8192 in passes of 4096 rows).
  *   other shapes: f16 MFMA on weights dequantised in registers.
  * Because the bias is removed from fp32 sums, codes equal to their zero-point
  * give outputs within rounding of 0 (about 2^-16 of s (1024 + z) sum|x| per
@@ -209,7 +209,7 @@ enum {
  * (no zero-point), any M >= 1: gfx950's fp4 / fp6 / fp8 -> f16 conversions give the
  * codes' exact values.  At M = 1 with K <= 16384, N <= 65536 the decode kernel runs (fp32
  * dot products of X with the values, s applied per group in fp32); at
- * 2 <= M <= 16 with G % 128 == 0, K <= 8192 the MFMA GEMV (f16 MFMA of X with
+ * 2 <= M <= 16 with G % 128 == 0 the MFMA GEMV (f16 MFMA of X with
  * the values, fp32 accumulation, s applied per 128-row step in fp32);
  * otherwise the qmm_gemm kernel (one rounding multiply by s, then f16 MFMA
  * with fp32 accumulation).  wq is qmm_pack's stream of the code bit
