@@ -910,11 +910,12 @@ def test_gemm_fp_decode_reads_every_code_exactly(q, orc, fmt):
 @pytest.mark.parametrize("fmt", FP_FORMATS)
 @pytest.mark.parametrize("M,K,N,G", [(2, 128, 17, 128), (8, 4096, 11008, 128), (16, 4096, 11008, 128),
                                      (16, 8192, 1000, 256),
-                                     (3, 1024, 300, 1024), (16, 8320, 40, 128)])
+                                     (3, 1024, 300, 1024), (16, 8320, 40, 128), (4, 12288, 70, 128)])
 def test_gemm_fp_batched_shapes(q, orc, fmt, M, K, N, G):
     """2 <= M <= 16 float-code products: one 128-row step with a ragged tile,
-    the 7B MLP shape at M 8, the longest K the MFMA GEMV takes, one group per
-    column, and K past it (the GEMM kernel)."""
+    the 7B MLP shape at M 8, the longest one-pass K of the MFMA GEMV, one
+    group per column, and K past it (passes of 4096 rows: a last pass of one
+    step per wave at K 8320, three passes at K 12288)."""
     bits = orc.FP_BITS[fmt]
     codes = fp_codes(fmt, K, N, 470 + fmt + K + M)
     c = synthetic.make_case(M, K, N, bits, G, 480 + fmt + K + M)
