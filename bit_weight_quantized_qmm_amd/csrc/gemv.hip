@@ -861,23 +861,43 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     // (MP: more than one pass; the one-pass form keeps the row scaling for the
     // epilogue and spends no registers on it inside the loop)
     const int KS = MMA_WAVES * S, P = MP ? (((R + 3) >> 2) + KS - 1) / KS : 1;
-    for (int pass = 0; pass < P; ++pass) {
-    const int tb = pass * KS;                       // first step of the pass
-    const int g0 = min(run_group(4 * tb, ginv), ng - 1);   // first group of the pass
-    if (pass > 0) __syncthreads();                  // the previous pass's table and row maxima are read
+    auto pass_g0 = [&](int pass) { return min(run_group(4 * pass * KS, ginv), ng - 1); };   // first group of a pass
 
     // s and z of the workgroup's columns: wave w reads columns w, w + 8, ...,
     // lane l holding group g0 + l (past ng, or past the workgroup's columns: zeros)
     constexpr int SZE = T * 16 / MMA_WAVES;
     uint32_t sraw[SZE], zraw[SZE];
+    auto load_sz = [&](int g0) {
 #pragma unroll
-    for (int e = 0; e < SZE; ++e) {
-        const int cl = wave + MMA_WAVES * e;
-        const uint32_t off = (g0 + lane < ng && cl < 16 * ntile)
-                                 ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)(g0 + lane)) * 2u : OOB;
-        sraw[e] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
-        zraw[e] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : zdef_bits;
+        for (int e = 0; e < SZE; ++e) {
+            const int cl = wave + MMA_WAVES * e;
+            const uint32_t off = (g0 + lane < ng && cl < 16 * ntile)
+                                     ? ((uint32_t)(16 * tile0 + cl) * (uint32_t)ng + (uint32_t)(g0 + lane)) * 2u : OOB;
+            sraw[e] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+            zraw[e] = PGZ ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : zdef_bits;
+        }
+    };
+    // X run of this lane for step t: row c, run 4 t + g (zeros past M or K)
+    auto load_xrun = [&](int t, uint32_t (&raw)[16]) {
+        const int run = 4 * t + g;
+        load_dwords<LOAD_DEFAULT>(xr, (run < R && c < M) ? ((uint32_t)c * K + (uint32_t)run * 32u) * 2u : OOB, raw, 16);
+    };
+    uint32_t xa[S][16];   // the wave's X runs of a pass
+    auto load_xa = [&](int tb) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) load_xrun(tb + wave * S + st, xa[st]);
+    };
+    // MP: a pass's s | z and X loads go out during the previous pass's stream
+    if constexpr (MP) {
+        load_sz(pass_g0(0));
+        load_xa(0);
     }
+
+    for (int pass = 0; pass < P; ++pass) {
+    const int tb = pass * KS;                       // first step of the pass
+    const int g0 = pass_g0(pass);
+    if (pass > 0) __syncthreads();                  // the previous pass's table and row maxima are read
+    if constexpr (!MP) load_sz(g0);
 
     // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c,
     // run 4 t + g of step t = wave * S + st.  Consecutive units walk one column
@@ -902,12 +922,6 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
         if (g0 + lane < ng) sz[lane * SZW + cl] = (sraw[e] & 0xffffu) | (zraw[e] << 16);
     }
 
-    // X run of this lane for step t: row c, run 4 t + g (zeros past M or K)
-    auto load_xrun = [&](int t, uint32_t (&raw)[16]) {
-        const int run = 4 * t + g;
-        load_dwords<LOAD_DEFAULT>(xr, (run < R && c < M) ? ((uint32_t)c * K + (uint32_t)run * 32u) * 2u : OOB, raw, 16);
-    };
-
     // A fragments and correction fragments of the wave's K slice, once: they
     // do not depend on the column tile.  Row c is first normalised by 2^e (its
     // maximum |x| over all of K taken across the 8 waves), so S1 and S2 stay
@@ -915,9 +929,7 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     half8_t A[S][4];
     uint32_t AC[S][2];   // correction fragment of lane group 0: (S1 hi, S1 lo), (S2 hi, S2 lo)
     {
-        uint32_t xa[S][16];
-#pragma unroll
-        for (int st = 0; st < S; ++st) load_xrun(tb + wave * S + st, xa[st]);
+        if constexpr (!MP) load_xa(tb);
         int erow = 0;
         if constexpr (FMT == 0) {
             uint32_t mx = 0;
@@ -974,6 +986,14 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
             p2[1] = s2l;
             AC[st][0] = g == 0 ? as_u32(p1) : 0u;
             AC[st][1] = g == 0 ? as_u32(p2) : 0u;
+        }
+    }
+    // the next pass's s | z and X runs load under this pass's stream (xa, sraw
+    // and zraw are free again: the fragments and the table are built)
+    if constexpr (MP) {
+        if (pass + 1 < P) {
+            load_sz(pass_g0(pass + 1));
+            load_xa(tb + KS);
         }
     }
 
@@ -1100,7 +1120,9 @@ __host__ __device__ constexpr int mma_ring(int bits) { return bits <= 3 || bits 
 template <int BITS, int S, int T, bool PGZ, int FMT, bool MP = false>
 static hipError_t gemv_mma_go(const GemvArgs &a, int grid, int tpw, hipStream_t st)
 {
-    constexpr int D0 = mma_ring(BITS);
+    // (the pass form holds the next pass's X runs during the stream: at most
+    // 4 units in flight there)
+    constexpr int D0 = MP && mma_ring(BITS) > 4 ? 4 : mma_ring(BITS);
     constexpr int D = D0 < S * T ? D0 : S * T;
     hipLaunchKernelGGL((gemv_mma_kernel<BITS, S, T, D, PGZ, FMT, MP>), dim3(grid), dim3(64 * MMA_WAVES), 0, st, a.X, a.wq, a.s, a.z, a.Y,
                        a.M, a.K, a.N, a.G, tpw);
@@ -1128,9 +1150,10 @@ static hipError_t gemv_mma_launch(const GemvArgs &a, hipStream_t st)
     const int tiles = (a.N + 15) / 16;
     const int tpw = std::min(8, std::max(1, (tiles + num_cus() - 1) / num_cus()));
     const int grid = (tiles + tpw - 1) / tpw;
-    if (steps > 8) {
+    if (steps > 8) {   // the pass form: at most 4 tiles per workgroup (its registers)
         if (tpw <= 2) return gemv_mma_go<BITS, 4, 2, PGZ, FMT, true>(a, grid, tpw, st);
-        return gemv_mma_go<BITS, 4, 8, PGZ, FMT, true>(a, grid, tpw, st);
+        const int tpw4 = std::min(tpw, 4);
+        return gemv_mma_go<BITS, 4, 4, PGZ, FMT, true>(a, (tiles + tpw4 - 1) / tpw4, tpw4, st);
     }
     if (steps <= 1) return gemv_mma_pick_t<BITS, 1, PGZ, FMT>(a, grid, tpw, st);
     if (steps <= 2) return gemv_mma_pick_t<BITS, 2, PGZ, FMT>(a, grid, tpw, st);
