@@ -461,6 +461,11 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
 {
     static_assert(BITS >= 1 && BITS <= 7, "q - z must fit a signed byte");
     constexpr int MS = 8, NS = 2;
+    // k = 1, 3, 4: a group's y += s * float(A) runs inside the next group's
+    // first MFMAs (below); k = 2 and k >= 5 keep it as a phase of its own (the
+    // fused form spilled there and measured slower: k 2 69.1 -> 70.8 us,
+    // k 7 103 -> 112 at M 2048, K = N = 4096)
+    constexpr bool FUSE = BITS <= 4 && BITS != 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * WG_RUNB];
     __shared__ uint16_t ssz[2][2][256];   // [buffer][s, z][column of the tile], fp16 bits
     int mt, nt;
@@ -516,13 +521,19 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
     };
 
     float y[MS][NS][4];
+    int4_t acc[MS][NS];   // the current group's sums
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int j = 0; j < NS; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[i][j][e] = 0.f;
-    int4_t acc[MS][NS];
+            for (int e = 0; e < 4; ++e) {
+                y[i][j][e] = 0.f;
+                acc[i][j][e] = 0;
+            }
+    // s of the group whose sums acc holds (FUSE: 0 before the first group,
+    // whose "previous group" then adds nothing)
+    float sc[NS] = {0.f, 0.f};
 
     XSet xa, xb;
     uint32_t wa[NS][BITS], wb[NS][BITS];
@@ -536,13 +547,33 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
     // lane (g, c) reads rows c + 16 ms of run g (16 ms leaves the XOR terms alone)
     const uint8_t *abase0[2] = {&lds[0][wg_xoff(c, g, 0)], &lds[0][wg_xoff(c, g, 1)]};
 
+    // y += s * float(A) of a finished group, for MFMA tile (ms, ns) (and the
+    // sums written out when asked for)
+    auto add_group = [&](int gi, int ms, int ns) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[ms][ns][i] = fmaf(sc[ns], (float)acc[ms][ns][i], y[ms][ns][i]);
+            if constexpr (DUMP) {
+                const int row = m0 + ms * 16 + 4 * g + i, col = wn0 + ns * 16 + c;
+                if (gi >= 0 && row < M && col < N) acc_out[((size_t)row * ng + gi) * N + col] = acc[ms][ns][i];
+            }
+        }
+    };
     // step tt: xin holds X(tt + 1), w the runs of step tt; afterwards they
     // receive X(tt + 3) and the runs of step tt + 2.  sched_barriers keep the
     // two steps of an iteration apart (their registers would otherwise be live
     // together), and the empty asm statements keep everything computed from
     // loaded values at its point of use (moved into the previous step, it
-    // would wait there for loads still in flight).
-    auto step = [&](int tt, bool first, XSet &xin, uint32_t (&w)[NS][BITS], float (&sc)[NS]) {
+    // would wait there for loads still in flight).  FUSE: the first step of
+    // group gi adds group gi - 1's sums to y tile by tile just before the MFMA
+    // that starts the tile's new sum, and scheduling groups interleave that
+    // VALU work with the MFMAs, so it runs beside the matrix core (as a phase
+    // of its own after a group's last MFMAs it is more than half of the
+    // loop's VALU instructions at G = 128).  M 2048, K = N = 4096, k 4:
+    // 66.2 -> 61.0 us (k 3: 77.0 -> 74.3, k 1: 69.0 -> 66.9; M 1024, k 4:
+    // 60.1 -> 54.7), Y bitwise the same.
+    auto step = [&](int tt, int gi, bool first, XSet &xin, uint32_t (&w)[NS][BITS]) __attribute__((always_inline)) {
+        float scn[NS];
         const int cur = tt & 1;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -559,7 +590,7 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
             for (int v = 0; v < 2; ++v)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bv[ns][v][e] = (int)((wka8_dword<BITS>(w[ns], 4 * v + e) + cz) ^ 0x80808080u);
-            if (first) sc[ns] = (float)as_half(ssz[cur][0][col]);
+            if (first) scn[ns] = (float)as_half(ssz[cur][0][col]);
         }
         load_w(tt + 2, w);
         const int bufoff = cur * (4 * WG_RUNB);
@@ -573,9 +604,25 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const int4_t zero4 = {0, 0, 0, 0};
+                    if (FUSE && first && v == 0) add_group(gi - 1, ms, ns);
                     acc[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ms], bv[ns][v],
                                                                         (first && v == 0) ? zero4 : acc[ms][ns], 0, 0, 0);
                 }
+        }
+        if (FUSE && first) {
+            // the dequantisation's VALU first, then one MFMA per 8 VALU
+            // (a tile's 4 conversions and 4 fmas), then the second half's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+#pragma unroll
+            for (int i = 0; i < MS * NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MS * NS, 0);
+        }
+        if (first) {
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) sc[ns] = scn[ns];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -586,29 +633,19 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto group_end = [&](int gi, const float (&sc)[NS]) {
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    y[ms][ns][i] = fmaf(sc[ns], (float)acc[ms][ns][i], y[ms][ns][i]);
-                    if constexpr (DUMP) {
-                        const int row = m0 + ms * 16 + 4 * g + i, col = wn0 + ns * 16 + c;
-                        if (row < M && col < N) acc_out[((size_t)row * ng + gi) * N + col] = acc[ms][ns][i];
-                    }
-                }
-    };
     // a group of SPG steps; step tt uses register set A when tt is even
-    auto group = [&](int gi, bool odd) {
-        float sc[NS];
+    auto group = [&](int gi, bool odd) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < SPG; ++j) {
-            if (((j & 1) != 0) == odd) step(gi * SPG + j, j == 0, xa, wa, sc);
-            else step(gi * SPG + j, j == 0, xb, wb, sc);
+            if (((j & 1) != 0) == odd) step(gi * SPG + j, gi, j == 0, xa, wa);
+            else step(gi * SPG + j, gi, j == 0, xb, wb);
         }
-        group_end(gi, sc);
+        if constexpr (!FUSE) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) add_group(gi, ms, ns);
+        }
     };
     if constexpr (SPG == 1) {
         int gi = 0;
@@ -619,6 +656,12 @@ __global__ __launch_bounds__(512) void w4a8_gemm_kernel(const int8_t *__restrict
         if (gi < ng) group(gi, false);
     } else {
         for (int gi = 0; gi < ng; ++gi) group(gi, false);
+    }
+    if constexpr (FUSE) {   // the last group's sums
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) add_group(ng - 1, ms, ns);
     }
 
 #pragma unroll
