@@ -379,14 +379,19 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
 }
 
 // Weight units in flight per wave (fastest measured on the 8B MLP shape at
-// k = 4: 4 against 1, 2 and 8).
+// k = 4: 4 against 1, 2 and 8, though within 4 %: 10.6 / 11.0 / 10.6 us at
+// 4 / 2 / 8).  k = 8 with at most 4 steps per wave (K <= 4096) takes 2: a unit
+// is twice the bytes, and M 16 / 8 / 1 measured 15.7 / 14.8 / 14.3 us with 4
+// against 14.7 / 14.1 / 13.9 with 2 (at K 8192, 26.7 against 27.3; k = 5..7
+// were slower with 2).
 constexpr int W4A8_RING = 4;
 
 template <int BITS, int S, int T, bool PGZ>
 static hipError_t w4a8_stream_go(const W4A8Args &a, dim3 grid, int tpw, hipStream_t st)
 {
     // a power of two that divides, or is a multiple of, the steps per tile
-    constexpr int D = S * T < W4A8_RING ? S * T : W4A8_RING;
+    constexpr int RING = BITS == 8 && S <= 4 ? 2 : W4A8_RING;
+    constexpr int D = S * T < RING ? S * T : RING;
     hipLaunchKernelGGL((w4a8_stream_kernel<BITS, S, T, D, PGZ>), grid, dim3(512), 0, st, a.Xq, a.sx, a.wq, a.s, a.z, a.Y,
                        a.acc, a.M, a.K, a.N, a.G, tpw);
     return hipGetLastError();
