@@ -701,10 +701,11 @@ GEMM8_M, GEMM8_N = 1100, 1800
 
 @pytest.mark.parametrize("bits", range(1, 8))
 @pytest.mark.parametrize("K,G,pgz", [(512, 128, False), (1024, 256, True), (1024, 512, False), (2048, 1024, True),
-                                     (1152, 128, True), (640, 128, False)])
+                                     (1152, 128, True), (640, 128, False), (128, 128, True), (256, 256, False)])
 def test_wka8_gemm_shapes(q, orc, bits, K, G, pgz):
     """The tiled int8 kernel: ragged M and N tiles, groups of 1, 2, 4 and 8 K
-    steps, an odd number of one-step groups (the loop's unpaired last step),
+    steps, an odd number of one-step groups (the loop's unpaired last step), a
+    single group (K = G: no group before it, its sums added after the loop),
     the default and per-group zero-points; int32 group sums bit-exact."""
     c = synthetic.make_w4a8_case(GEMM8_M, K, GEMM8_N, G, synthetic.seed_for(99, bits, K // G), bits=bits,
                                  per_group_z=pgz)
