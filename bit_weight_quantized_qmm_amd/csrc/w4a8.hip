@@ -302,11 +302,12 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
 
     // UT tiles per loop iteration keep every ring slot a compile-time index
     constexpr int UT = D > S ? D / S : 1;
-    // the tile loop, compiled twice: SP1 (G = 128, every step ends its group:
-    // no running sums) and the general case; a uniform branch picks one
+    // the tile loop, compiled for SP1 (G = 128, every step ends its group: no
+    // running sums) or the general case, each with and without the dump of the
+    // sums; uniform branches pick one
     const int lsp = __builtin_ctz((unsigned)sp);   // sp = G / 128 is a power of two
-    auto tiles_loop = [&](auto sp1_tag) {
-        constexpr bool SP1 = decltype(sp1_tag)::value;
+    auto tiles_loop = [&](auto sp1_tag, auto dump_tag) {
+        constexpr bool SP1 = decltype(sp1_tag)::value, DUMP = decltype(dump_tag)::value;
 #pragma unroll 1
         for (int jb = 0; jb < ntile; jb += UT) {
 #pragma unroll
@@ -315,6 +316,26 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                 float4_t y = float4_t{0.f, 0.f, 0.f, 0.f};
                 int4_t graw = {0, 0, 0, 0}, gsx = {0, 0, 0, 0};
                 const int n = 16 * (tile0 + j) + c;
+                // y += s * A of a finished group (a step past K adds nothing:
+                // its sums are zero and its s is replaced by 0)
+                auto end_group = [&](const int4_t &A, float sc, int t, int grp) __attribute__((always_inline)) {
+                    if constexpr (DUMP) {   // the exact group sums, for callers that ask
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 4 * g + i;
+                            if (t < TT && row < mrows && j < ntile && n < N)
+                                acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A[i];
+                        }
+                    }
+                    const float scv = t < TT ? sc : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = fmaf(scv, (float)A[i], y[i]);
+                };
+                // SP1: a step's group end runs after the next step's MFMAs are
+                // issued, so it does not wait for its own MFMAs' results
+                int4_t Ap = {0, 0, 0, 0};
+                float scp = 0.f;
+                int tp = 0;
 #pragma unroll
                 for (int st = 0; st < S; ++st) {
                     const int slot = (jj * S + st) % D;
@@ -333,36 +354,36 @@ __global__ __launch_bounds__(512) void w4a8_stream_kernel(const int8_t *__restri
                     const float sc = (float)as_half((uint16_t)(szv & 0xffffu));
                     // refill the slot with the unit D ahead (past the tiles: no load)
                     issue(jb + (jj * S + st + D) / S, (jj * S + st + D) % S, slot);
-                    // the group's int32 sums A, scaled into y when the group ends
-                    // with this step
-                    if (!SP1) {
+                    if constexpr (SP1) {
+                        if (st > 0) end_group(Ap, scp, tp, tp);
+                        Ap = raw - zz * sxg[st];
+                        scp = sc;
+                        tp = t;
+                    } else {
+                        // the group's int32 sums A, scaled into y when the group
+                        // ends with this step
                         graw += raw;
                         gsx += sxg[st];
-                    }
-                    if ((SP1 || ((t + 1) & (sp - 1)) == 0) && t < TT) {
-                        const int4_t A = SP1 ? raw - zz * sxg[st] : graw - zz * gsx;
-                        if (dump) {   // the exact group sums, for callers that ask
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int row = 4 * g + i;
-                                if (row < mrows && j < ntile && n < N) acc_out[((size_t)(m0 + row) * ng + grp) * N + n] = A[i];
-                            }
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) y[i] = fmaf(sc, (float)A[i], y[i]);
-                        if (!SP1) {
+                        if (((t + 1) & (sp - 1)) == 0) {
+                            end_group(graw - zz * gsx, sc, t, grp);
                             graw = int4_t{0, 0, 0, 0};
                             gsx = int4_t{0, 0, 0, 0};
                         }
                     }
                 }
+                if constexpr (SP1) end_group(Ap, scp, tp, tp);
                 // lane (g, c) of a tile holds rows 4g..4g+3, column c
                 *reinterpret_cast<float4_t *>(&red[wave][j][lane][0]) = y;
             }
         }
     };
-    if (sp == 1) tiles_loop(std::true_type{});
-    else tiles_loop(std::false_type{});
+    if (sp == 1) {
+        if (dump) tiles_loop(std::true_type{}, std::true_type{});
+        else tiles_loop(std::true_type{}, std::false_type{});
+    } else {
+        if (dump) tiles_loop(std::false_type{}, std::true_type{});
+        else tiles_loop(std::false_type{}, std::false_type{});
+    }
     __syncthreads();
     for (int o = threadIdx.x; o < ntile * 256; o += 512) {
         const int j = o >> 8, m = (o >> 4) & 15, col = o & 15;
