@@ -158,8 +158,6 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
     uint32_t raw[QR_MAXR][VEC == 4 ? 2 : 1];
     float lo[VEC], hi[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) lo[v] = hi[v] = 0.f;
-#pragma unroll
     for (int r = 0; r < QR_MAXR; ++r) {
         if (r < rp && live) {   // uniform in r; live per lane
             const size_t at = base + (size_t)r * N;
@@ -175,16 +173,28 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
             for (int e = 0; e < (VEC == 4 ? 2 : 1); ++e) raw[r][e] = 0u;
         }
     }
+    // the range on fp16 pairs (min and max pick one of their operands, so
+    // fp16 and fp32 give the same values): one packed op per two codes, no
+    // conversions; a lone column (VEC 1) uses the pair's low half
+    constexpr int NP = VEC == 4 ? 2 : 1;
+    half2_t lo2[NP], hi2[NP];
+#pragma unroll
+    for (int e = 0; e < NP; ++e) lo2[e] = hi2[e] = half2_t{(_Float16)0.0f, (_Float16)0.0f};
 #pragma unroll
     for (int r = 0; r < QR_MAXR; ++r) {
         if (r < rp) {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const float w = VEC == 4 ? (float)as_half2(raw[r][v >> 1])[v & 1] : (float)as_half((uint16_t)raw[r][0]);
-                lo[v] = fminf(lo[v], w);
-                hi[v] = fmaxf(hi[v], w);
+            for (int e = 0; e < NP; ++e) {
+                const half2_t w2 = as_half2(raw[r][e]);
+                lo2[e] = __builtin_elementwise_min(lo2[e], w2);
+                hi2[e] = __builtin_elementwise_max(hi2[e], w2);
             }
         }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        lo[v] = (float)lo2[v >> 1][v & 1];
+        hi[v] = (float)hi2[v >> 1][v & 1];
     }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
