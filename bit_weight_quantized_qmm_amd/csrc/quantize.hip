@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
             const float q = fminf(fmaxf(round_quotient(w[v], sg[v], inv[v], half[v]) + zg[v], 0.f), QMAX);
-            packed |= (uint32_t)q << (8 * v);
+            packed = __builtin_amdgcn_cvt_pk_u8_f32(q, v, packed);   // byte v of the word, one op
         }
         const size_t at = base + (size_t)r * N;
         if constexpr (VEC == 4)
@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
             for (int v = 0; v < VEC; ++v) {
                 const float w = VEC == 4 ? (float)as_half2(raw[r][v >> 1])[v & 1] : (float)as_half((uint16_t)raw[r][0]);
                 const float q = fminf(fmaxf(round_quotient(w, sg[v], inv[v], half[v]) + zg[v], 0.f), QMAX);
-                packed |= (uint32_t)q << (8 * v);
+                // q is a whole number in 0..255: convert and insert byte v in one op
+                packed = __builtin_amdgcn_cvt_pk_u8_f32(q, v, packed);
             }
             const size_t at = base + (size_t)r * N;
             if constexpr (VEC == 4)
