@@ -42,7 +42,8 @@ __device__ __forceinline__ _Float16 fp16_of_double(double x)
 // answer except at an exact tie, wherever |w / s| <= 256.5 (off a tie,
 // w / s lies at least about 2^-13 from a half-integer there, far more than
 // the fp32 product's error); at a tie the residual w - t s from one fma is
-// exactly +-s / 2, and an odd t moves one step toward it.  Beyond 256.5 the
+// exactly +-s / 2, and the answer is the even one of t and t + sign(r),
+// 2 rint(t / 2 + sign(r) / 4) (no integer test of t).  Beyond 256.5 the
 // result can be off but stays past +-255 on the quotient's side, so every
 // code, clamped to 0..2^k - 1 after adding z <= 255, is the same.  Checked
 // for every finite fp16 w and every positive fp16 s on the host.
@@ -50,8 +51,8 @@ __device__ __forceinline__ float round_quotient(float w, float s, float inv, flo
 {
     const float t = __builtin_rintf(w * inv);
     const float r = __builtin_fmaf(-t, s, w);
-    const bool fix = (__builtin_fabsf(r) == half) & (((int)t & 1) != 0);
-    return fix ? t + __builtin_copysignf(1.0f, r) : t;   // t itself otherwise (keeps a -0)
+    const float even = 2.0f * __builtin_rintf(__builtin_fmaf(t, 0.5f, __builtin_copysignf(0.25f, r)));
+    return __builtin_fabsf(r) == half ? even : t;   // t itself off a tie (keeps a -0)
 }
 
 template <int BITS, int VEC>

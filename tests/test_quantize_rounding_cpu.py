@@ -2,8 +2,8 @@
 
 The kernels take round(w / s), ties to even (BitLLM Sec. 2.2, eq. (1)), as
 t = rint(w * inv) with inv = 1 / s rounded to fp32, then fix only an exact
-tie: the residual r = w - t s from one fma equals +-s / 2 there, and an odd t
-moves one step toward r.  The claim is that every code the kernel can form,
+tie: the residual r = w - t s from one fma equals +-s / 2 there, and the
+result is the even one of t and t + sign(r), 2 rint(t / 2 + sign(r) / 4).  The claim is that every code the kernel can form,
 clamp(round + z, 0, 2^k - 1) with 0 <= z <= 255, is then the same as with the
 exact quotient, for every finite fp16 w and every positive fp16 s: equal
 rounding wherever |w / s| <= 256.5, and beyond that a result past +-255 on
@@ -24,11 +24,14 @@ def kernel_round(w32, w64, s16, tie_fix=True):
     inv = np.float32(1.0) / s32
     half = np.float32(0.5) * s32
     t = np.rint(w32 * inv)
-    r = (w64 - t.astype(np.float64) * s64).astype(np.float32)
-    odd = (np.clip(t, -2.0 ** 31, 2.0 ** 31 - 1).astype(np.int64) & 1) != 0
     if not tie_fix:
         return t
-    return np.where((np.abs(r) == half) & odd, t + np.sign(r), t)
+    r = (w64 - t.astype(np.float64) * s64).astype(np.float32)
+    # at a tie, the even one of t and t + sign(r): 2 rint(t / 2 + sign(r) / 4),
+    # the inner step one fma rounded to float32
+    q4 = (t.astype(np.float64) * 0.5 + np.copysign(0.25, r).astype(np.float64)).astype(np.float32)
+    even = np.float32(2.0) * np.rint(q4)
+    return np.where(np.abs(r) == half, even, t)
 
 
 def mismatches(tie_fix=True, step=1):
