@@ -142,7 +142,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
 // codes come from the registers (W is read once: the two-pass kernel above
 // reads it twice).
 constexpr int QR_MAXR = 16;   // rows per lane: G <= 256
-template <int BITS, int VEC>
+// RPT > 0: G / 16 == RPT known at compile time (G = 128: 8 rows per lane), so
+// the row loops carry no per-row branches
+template <int BITS, int VEC, int RPT = 0>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ W, uint8_t *__restrict__ codes,
                                                             uint16_t *__restrict__ s, uint16_t *__restrict__ z, int K,
                                                             int N, int G)
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
     const int c = lane & 15, part = tid >> 4;   // part 0..15
     const int n0 = (blockIdx.x * 16 + c) * VEC;
     const bool live = n0 < N;
-    const int g = blockIdx.y, ng = K / G, rp = G >> 4;
+    const int g = blockIdx.y, ng = K / G, rp = RPT > 0 ? RPT : G >> 4;
     constexpr float QMAX = (float)((1 << BITS) - 1);
     const size_t base = ((size_t)g * G + (size_t)part * rp) * N + n0;
 
@@ -259,7 +261,9 @@ hipError_t launch_quantize(const uint16_t *W, uint8_t *codes, uint16_t *s, uint1
     const dim3 block(256), grid((unsigned)((N + per_block - 1) / per_block), (unsigned)(K / G));
 #define QMM_Q(B)                                                                                                \
     do {                                                                                                        \
-        if (one_pass && vec)                                                                                    \
+        if (one_pass && vec && G == 128)                                                                        \
+            hipLaunchKernelGGL((quantize_rows_kernel<B, 4, 8>), grid, block, 0, st, W, codes, s, z, K, N, G);   \
+        else if (one_pass && vec)                                                                               \
             hipLaunchKernelGGL((quantize_rows_kernel<B, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);      \
         else if (one_pass)                                                                                      \
             hipLaunchKernelGGL((quantize_rows_kernel<B, 1>), grid, block, 0, st, W, codes, s, z, K, N, G);      \

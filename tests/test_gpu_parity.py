@@ -620,12 +620,13 @@ def check_quantize(q, orc, W, bits, G):
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
-@pytest.mark.parametrize("K,N,G", [(256, 300, 64), (1024, 70, 128), (96, 513, 32), (480, 132, 96), (1600, 77, 160),
-                                   (512, 260, 256), (1024, 68, 512), (2048, 33, 1024)])
+@pytest.mark.parametrize("K,N,G", [(256, 300, 64), (1024, 70, 128), (1024, 196, 128), (96, 513, 32), (480, 132, 96),
+                                   (1600, 77, 160), (512, 260, 256), (1024, 68, 512), (2048, 33, 1024)])
 def test_quantize_small(q, orc, bits, K, N, G):
     """Codes, s and z bit-exact on LLM-like weights: several column blocks and
     a ragged column tail; groups of 2 to 16 rows per lane in the one-pass
-    kernel (G 32 .. 256, odd counts at G 96 and 160) and the two-pass kernel
+    kernel (G 32 .. 256, odd counts at G 96 and 160; G 128 with N a multiple
+    of 4 takes its form compiled for 8 rows per lane) and the two-pass kernel
     beyond (G 512, 1024)."""
     rng = np.random.default_rng(synthetic.seed_for(99, bits, K + N))
     W = rng.normal(0.0, 0.02, (K, N)).astype(np.float16)
@@ -633,11 +634,13 @@ def test_quantize_small(q, orc, bits, K, N, G):
     check_quantize(q, orc, W, bits, G)
 
 
+@pytest.mark.parametrize("G", [32, 128])
 @pytest.mark.parametrize("bits", [1, 2, 4, 8])
-def test_quantize_special_groups(q, orc, bits):
+def test_quantize_special_groups(q, orc, bits, G):
     """Constant groups (zero, positive, negative), a range past the fp16 scale, a
-    scale that underflows, exact rounding ties, and the largest fp16 values."""
-    K, N, G = 128, 260, 32
+    scale that underflows, exact rounding ties, and the largest fp16 values
+    (at G 128 a column's special rows share one group)."""
+    K, N = 128, 260
     rng = np.random.default_rng(41 + bits)
     W = rng.normal(0.0, 0.05, (K, N)).astype(np.float16)
     W[0:32, 1] = 0
