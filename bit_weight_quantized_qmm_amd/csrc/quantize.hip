@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
 // codes come from the registers (W is read once: the two-pass kernel above
 // reads it twice).
 constexpr int QR_MAXR = 16;   // rows per lane: G <= 256
-// RPT > 0: G / 16 == RPT known at compile time (G = 128: 8 rows per lane), so
-// the row loops carry no per-row branches
+// RPT > 0: G / 16 == RPT known at compile time (G = 64, 128, 256: 4, 8, 16
+// rows per lane), so the row loops carry no per-row branches
 template <int BITS, int VEC, int RPT = 0>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ W, uint8_t *__restrict__ codes,
                                                             uint16_t *__restrict__ s, uint16_t *__restrict__ z, int K,
@@ -263,6 +263,10 @@ hipError_t launch_quantize(const uint16_t *W, uint8_t *codes, uint16_t *s, uint1
     do {                                                                                                        \
         if (one_pass && vec && G == 128)                                                                        \
             hipLaunchKernelGGL((quantize_rows_kernel<B, 4, 8>), grid, block, 0, st, W, codes, s, z, K, N, G);   \
+        else if (one_pass && vec && G == 64)                                                                    \
+            hipLaunchKernelGGL((quantize_rows_kernel<B, 4, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);   \
+        else if (one_pass && vec && G == 256)                                                                   \
+            hipLaunchKernelGGL((quantize_rows_kernel<B, 4, 16>), grid, block, 0, st, W, codes, s, z, K, N, G);  \
         else if (one_pass && vec)                                                                               \
             hipLaunchKernelGGL((quantize_rows_kernel<B, 4>), grid, block, 0, st, W, codes, s, z, K, N, G);      \
         else if (one_pass)                                                                                      \
