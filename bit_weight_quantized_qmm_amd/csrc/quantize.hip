@@ -7,8 +7,9 @@
 //   lo = min(0, min w),  hi = max(0, max w)
 //   s  = fp16((hi - lo) / (2^k - 1)),  1 if that is 0,  65504 if it overflows
 //   z  = clamp(round(-lo / s), 0, 2^k - 1),  q = clamp(round(w / s) + z, 0, 2^k - 1)
-// Every rounding decision is the one the exact quotient gives
-// (round_quotient).  The codes feed qmm_pack.
+// Every code and zero-point is the one the exact quotient gives
+// (round_quotient rounds exactly wherever the result can change one).  The
+// codes feed qmm_pack.
 //
 // Two kernels.  Groups of at most 256 rows (quantize_rows_kernel): one pass
 // over W, each lane holding G / 16 rows in registers.  Larger groups
