@@ -897,7 +897,11 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     const int tb = pass * KS;                       // first step of the pass
     const int g0 = pass_g0(pass);
     if (pass > 0) __syncthreads();                  // the previous pass's table and row maxima are read
-    if constexpr (!MP) load_sz(g0);
+    if constexpr (!MP) {
+        // X first: its round trip then overlaps the s | z table's
+        load_xa(tb);
+        load_sz(g0);
+    }
 
     // weights of unit (tile j, step st) for lane (g, c): column 16 (tile) + c,
     // run 4 t + g of step t = wave * S + st.  Consecutive units walk one column
@@ -929,7 +933,6 @@ __global__ __launch_bounds__(64 * MMA_WAVES) void gemv_mma_kernel(const uint16_t
     half8_t A[S][4];
     uint32_t AC[S][2];   // correction fragment of lane group 0: (S1 hi, S1 lo), (S2 hi, S2 lo)
     {
-        if constexpr (!MP) load_xa(tb);
         int erow = 0;
         if constexpr (FMT == 0) {
             uint32_t mx = 0;
