@@ -3,13 +3,14 @@
 The kernels take round(w / s), ties to even (BitLLM Sec. 2.2, eq. (1)), as
 t = rint(w * inv) with inv = 1 / s rounded to fp32, then fix only an exact
 tie: the residual r = w - t s from one fma equals +-s / 2 there, and the
-result is the even one of t and t + sign(r), 2 rint(t / 2 + sign(r) / 4).  The claim is that every code the kernel can form,
-clamp(round + z, 0, 2^k - 1) with 0 <= z <= 255, is then the same as with the
-exact quotient, for every finite fp16 w and every positive fp16 s: equal
-rounding wherever |w / s| <= 256.5, and beyond that a result past +-255 on
-the quotient's side.  numpy's float32 multiply and rint round to nearest even
-like v_mul_f32 and v_rndne_f32; the fma is a float64 product and sum (exact
-for these operands) rounded once to float32; v_cvt_i32_f32 saturates.
+result is the even one of t and t + sign(r), 2 rint(t / 2 + sign(r) / 4).
+The claim is that every code the kernel can form, clamp(round + z, 0,
+2^k - 1) with 0 <= z <= 255, is then the same as with the exact quotient,
+for every finite fp16 w and every positive fp16 s: equal rounding wherever
+|w / s| <= 256.5, and beyond that a result past +-255 on the quotient's
+side.  numpy's float32 multiply and rint round to nearest even like v_mul_f32
+and v_rndne_f32; each fma is a float64 product and sum (exact for these
+operands) rounded once to float32.
 """
 import numpy as np
 import pytest
