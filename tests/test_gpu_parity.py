@@ -482,6 +482,12 @@ def run_w4a8(q, c, with_acc=True):
     return Y, acc
 
 
+def same_without_dump(Y, Y2):
+    """The kernels are compiled with and without the dump of the int32 sums;
+    both must produce the same Y bit for bit."""
+    assert torch.equal(Y.cpu().view(torch.int16), Y2.cpu().view(torch.int16))
+
+
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 33])
 @pytest.mark.parametrize("G,pgz", [(128, False), (128, True), (256, True)])
 def test_w4a8_small(q, orc, M, G, pgz):
@@ -491,6 +497,7 @@ def test_w4a8_small(q, orc, M, G, pgz):
     A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], c["z"], G)
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
     assert rel_err(Y, ref) <= TOL
+    same_without_dump(Y, run_w4a8(q, c, with_acc=False)[0])
 
 
 @pytest.mark.parametrize("M,K,N,G,pgz", [(3, 2048, 50, 512, True), (16, 2048, 33, 1024, False),
@@ -504,6 +511,7 @@ def test_w4a8_shapes(q, orc, M, K, N, G, pgz):
     A, ref = orc.w4a8(c["Xq"], c["sx"], orc.pack(c["codes"], 4), c["s"], c["z"], G)
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), A)
     assert rel_err(Y, ref) <= TOL
+    same_without_dump(Y, run_w4a8(q, c, with_acc=False)[0])
 
 
 def test_w4a8_extreme_activations(q, orc):
@@ -556,6 +564,7 @@ def test_wka8_small(q, orc, bits, M, G, pgz):
     c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(97, bits, M + G), bits=bits, per_group_z=pgz)
     Y, acc = run_wka8(q, c, bits)
     check_wka8(orc, c, bits, Y, acc)
+    same_without_dump(Y, run_wka8(q, c, bits, with_acc=False)[0])
 
 
 @pytest.mark.parametrize("bits,M,K,N,G,pgz", [(8, 3, 2048, 50, 512, True), (3, 16, 2048, 33, 1024, False),
@@ -568,6 +577,7 @@ def test_wka8_shapes(q, orc, bits, M, K, N, G, pgz):
     c = synthetic.make_w4a8_case(M, K, N, G, synthetic.seed_for(98, bits, M), bits=bits, per_group_z=pgz)
     Y, acc = run_wka8(q, c, bits)
     check_wka8(orc, c, bits, Y, acc)
+    same_without_dump(Y, run_wka8(q, c, bits, with_acc=False)[0])
 
 
 @pytest.mark.parametrize("bits", [2, 5, 8])
@@ -589,6 +599,7 @@ def test_wka8_extreme(q, orc, bits, K, G):
     c["s"] = (c["s"].astype(np.float32) / (1 << e)).astype(np.float16)
     Y, acc = run_wka8(q, c, bits)
     check_wka8(orc, c, bits, Y, acc)
+    same_without_dump(Y, run_wka8(q, c, bits, with_acc=False)[0])
 
 
 def test_wka8_four_bits_is_w4a8(q):
